@@ -1,0 +1,223 @@
+"""Benchmark of the paged fused-MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+
+Workload (default): the Qwen3-30B-A3B-shaped decode layer -- 64 tokens,
+128 experts, top-8, hidden 2048, inter 768, bf16 weights on one 3 MiB page per
+projection at seeded positions of a 4 GiB pool interleaved with KV blocks.
+Inputs are synthetic and resident in HBM before timing starts. One step is
+one call of the whole layer (gating, count, sort, gate/up GEMM, down GEMM,
+combine). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "paged_moe_expert_amd", "csrc", "moe_kernels.hip")
+STAGES = ["gating", "count", "sort", "gemm_up", "gemm_down", "combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def traffic_from_profiles(workload: str, kernel: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, xb, lg, wb, n_tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.layout import Layout, build_pool
+    from oracle.moe import moe_forward
+    lay = Layout(cfg).run()
+    pt = lay.page_table()
+    pool = build_pool(cfg, pt, wb, poison=False)
+    toks = np.arange(n_tokens)
+    t0 = time.perf_counter()
+    moe_forward(xb, lg, pool, pt, cfg.page_bytes, E=cfg.E, k=cfg.k, H=cfg.H, I=cfg.I,
+                dtype=cfg.dtype, tokens=toks)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tokens} of {cfg.T} tokens (routing over all {cfg.T}), fp64 numpy, "
+                      f"page resolution included; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=0, help="override T (decode sweep)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the paged fused-MoE layer runs on a single "
+              "MI355X here and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_inputs import CONFIGS, gen
+    from paged_moe_expert_amd import rimuru as R
+    from paged_moe_expert_amd.layouts import DeviceLayout
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.config]
+    T = args.tokens or cfg.T
+    dev = torch.device("cuda:0")
+    log(f"[bench] {cfg.name}: T={T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} {cfg.dtype} "
+        f"page={cfg.page_bytes} pool={cfg.pool_bytes >> 20} MiB")
+
+    # ---- layout and device-resident inputs (untimed)
+    t0 = time.perf_counter()
+    pt = DeviceLayout(cfg).run().page_table()
+    wb = gen.all_weight_bits(cfg)
+    xb, lg = gen.x_bits(cfg, T), gen.logits(cfg, T)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    idt = np.int16 if cfg.dtype == "bf16" else np.int32
+    wdev = torch.from_numpy(wb.view(idt)).to(dev)
+    pool = torch.empty(cfg.pool_bytes, dtype=torch.uint8, device=dev)
+    pool.view(torch.int32).fill_(0x7FC07FC0)
+    ptd = torch.from_numpy(pt).to(dev)
+    R.experts_store(pool, ptd, wdev, cfg.page_bytes)
+    del wdev
+    x = torch.from_numpy(xb.view(idt)).to(dev).view(tdt)
+    lgd = torch.from_numpy(lg).to(dev)
+    dt_code = R.BF16 if cfg.dtype == "bf16" else R.F32
+    bufs = R.MoeBuffers(T, cfg.E, cfg.k, cfg.H, cfg.I, dt_code, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t0:.1f} s")
+
+    def step(events=None):
+        R.fused_moe_paged(x, lgd, pool, ptd, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs,
+                          stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    evs = [[R.event_create() for _ in range(R.MOE_STAGES + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.zeros((args.steps, R.MOE_STAGES))
+    for s in range(args.steps):
+        for i in range(R.MOE_STAGES):
+            stage_ms[s, i] = R.event_elapsed_ms(evs[s][i], evs[s][i + 1])
+    for row in evs:
+        for e in row:
+            R.event_destroy(e)
+    log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+
+    # ---- algorithmic work of this input
+    off = bufs.expert_off.cpu().numpy()
+    srt = bufs.sorted_ids.cpu().numpy()
+    TK = T * cfg.k
+    counts = np.array([int(np.sum(srt[off[e]:off[e + 1]] < TK)) for e in range(cfg.E)])
+    touched = int(np.sum(counts > 0))
+    es = cfg.es
+    HI = cfg.H * cfg.I
+    w_bytes = touched * 3 * HI * es
+    io_bytes = T * cfg.H * es * 2 + T * cfg.E * 4
+    flops = 6.0 * HI * TK
+    up_bytes = touched * 2 * HI * es + T * cfg.H * es + TK * cfg.I * es
+    up_flops = 4.0 * HI * TK
+
+    ms_step = wall * 1e3 / args.steps
+    med = np.median(stage_ms, axis=0)
+    mean = stage_ms.mean(axis=0)
+    up_ms = float(mean[3])
+    decode_like = (w_bytes + io_bytes) / HBM_PEAK_GBS > flops / (BF16_PEAK_TFLOPS * 1e3)
+    if decode_like:
+        achieved = up_bytes / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "gemm_up", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles(cfg.name, "gemm_up"),
+                "algorithmic_bytes_per_launch": up_bytes, "avg_launch_us": round(up_ms * 1e3, 2)}
+    else:
+        achieved = up_flops / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_up", "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles(cfg.name, "gemm_up"),
+                "algorithmic_flops_per_launch": up_flops, "avg_launch_us": round(up_ms * 1e3, 2)}
+
+    out = {
+        "metric": "paged fused-MoE tokens/s + TFLOP/s (or HBM GB/s) as % of MI355X roofline",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I,
+                   "page_bytes": cfg.page_bytes, "pool_bytes": cfg.pool_bytes,
+                   "experts_touched": touched, "block_m": bufs.block_m},
+        "layer": {"tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+                  "hbm_gbs": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9, 1),
+                  "algorithmic_bytes": w_bytes + io_bytes, "algorithmic_flops": flops,
+                  "hbm_frac": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "stages_us_median": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, med)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(cfg.with_T(T), xb, lg, wb, min(args.cpu_tokens, T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

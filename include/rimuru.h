@@ -1,0 +1,263 @@
+/*
+ * rimuru.h -- C ABI of the paged fused-MoE library (librimuru.so) for MI355X.
+ *
+ * The library has two halves:
+ *
+ *  1. A host-side page allocator over one shared page pool, with one memory
+ *     view per tensor type. Rimuru paper summary ("Rimuru: Unified Memory
+ *     Management for Modern LLM Serving via Elastic Expert Offloading",
+ *     thelatestinai.com), abstract and Figures 6-7; explainer "Rimuru unifies
+ *     serving memory" (learnaivisually.com), paragraph on moving the fence.
+ *     The allocator only hands out byte offsets; it never touches device
+ *     memory.
+ *
+ *  2. The page-table-aware fused MoE layer: routing (softmax top-k,
+ *     renormalised), grouping of routed slots by expert, and the gated SiLU
+ *     expert MLP with a weighted top-k combine, reading every expert weight
+ *     in place through the expert view's page table, never copying an expert
+ *     into a contiguous buffer (paper summary, abstract; explainer, paragraph
+ *     on the two pieces that make the moving fence usable; Figure 11's
+ *     "Discrete FusedMoE").
+ *
+ * Conventions for every call:
+ *  - Every function returns a status; 0 is success, negative values are the
+ *    RIMURU_E* codes below. rimuru_last_error() returns a thread-local
+ *    message for the last failing call on the calling thread.
+ *  - Nothing crosses this ABI but C types, plain host pointers, device
+ *    pointers given as void* / typed pointers, and hipStream_t given as void*.
+ *    No exception escapes; the library never aborts the process.
+ *  - Device memory is always owned by the caller. The library never
+ *    allocates or frees device memory.
+ *  - Host objects (pools and views) are owned by the library between their
+ *    create call and rimuru_pool_destroy(). A pool and its views must not
+ *    be used from two threads at once.
+ */
+#ifndef RIMURU_H
+#define RIMURU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rimuru_status;
+
+enum {
+  RIMURU_OK = 0,
+  RIMURU_EINVAL = -1, /* bad argument, unknown owner, double free */
+  RIMURU_ENOMEM = -2, /* pool exhausted or a view budget exceeded */
+  RIMURU_ERANGE = -3, /* a page-table entry outside the pool (checked call) */
+  RIMURU_EDTYPE = -4, /* unsupported element type */
+  RIMURU_EHIP = -5,   /* a HIP runtime call failed (launch, event) */
+  RIMURU_EBUSY = -6   /* a budget change would cut into resident pages */
+};
+
+enum { RIMURU_F32 = 0, RIMURU_BF16 = 1 };
+
+/* Tensor types that own a view (Table 1 of the paper summary: expert
+ * projections, KV cache, SSM state, conv state). */
+enum { RIMURU_VIEW_EXPERT = 0, RIMURU_VIEW_KV = 1, RIMURU_VIEW_SSM = 2, RIMURU_VIEW_CONV = 3 };
+
+typedef struct rimuru_pool rimuru_pool; /* opaque, host side */
+typedef struct rimuru_view rimuru_view; /* opaque, host side */
+
+/* Thread-local text for the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next failing call on the same thread. */
+const char* rimuru_last_error(void);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int32_t rimuru_abi_version(void);
+#define RIMURU_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------ */
+/* Page pool and views                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Create host state for a shared page pool of pool_bytes bytes cut into
+ * floor(pool_bytes / huge_page_bytes) huge pages (paper summary, abstract:
+ * a shared page pool with huge-page alignment; explainer: huge pages are a
+ * common multiple of the expert and state page sizes). Bytes past the last
+ * whole huge page are unused and reported as waste.
+ *   huge_page_bytes: > 0, a multiple of 128, <= pool_bytes.
+ *   out: receives the pool; free it with rimuru_pool_destroy().
+ * Errors: EINVAL. */
+rimuru_status rimuru_pool_create(uint64_t pool_bytes, uint64_t huge_page_bytes,
+                                 rimuru_pool** out);
+
+/* Destroy a pool and every view mapped on it. NULL is a no-op. */
+rimuru_status rimuru_pool_destroy(rimuru_pool* pool);
+
+/* Register a memory view: one tensor type's own page size over the shared
+ * pool (paper summary, abstract and Figure 6).
+ *   kind: RIMURU_VIEW_*.
+ *   page_bytes: > 0, a multiple of 128.
+ *   parent: NULL to cut this view's pages straight from huge pages
+ *     (page_bytes must then divide huge_page_bytes), or another view of the
+ *     same pool whose pages are split into pages of this one (page_bytes <=
+ *     the parent's page size; floor(parent / page) pages per parent page,
+ *     the rest is waste). Figure 7: huge -> expert-sized -> KV-sized.
+ *   A KV view may not be cut straight from huge pages unless its page is a
+ *   whole huge page (explainer: a huge page is never cut straight into KV
+ *   blocks).
+ *   out: receives the view, owned by the pool.
+ * A new view has no budget limit.
+ * Errors: EINVAL. */
+rimuru_status rimuru_view_map(rimuru_pool* pool, int32_t kind, uint64_t page_bytes,
+                              rimuru_view* parent, rimuru_view** out);
+
+/* Allocate n_pages pages of view v for one owner (a request, or one expert
+ * projection) and write their pool byte offsets, in allocation order, to
+ * out_offsets[0..n_pages). Owner ids >= 2^63 are reserved. Calling again for
+ * the same owner appends pages.
+ * Placement, one page at a time: the lowest-address parent page of v that
+ * already holds a page of this owner and has a free slot; else the
+ * lowest-address parent with a free slot; else a new parent (the
+ * lowest-address free huge page, or a page of the parent view allocated by
+ * these same rules). Within a parent, the lowest free slot (explainer: one
+ * request's small pages are cut from the same parent when possible).
+ * All or nothing: on failure the pool is left exactly as it was.
+ * Errors: EINVAL (n_pages == 0, reserved owner, NULL out_offsets),
+ *         ENOMEM (no room, or the view's budget would be exceeded). */
+rimuru_status rimuru_view_alloc(rimuru_view* v, uint64_t owner, uint64_t n_pages,
+                                int64_t* out_offsets);
+
+/* Free every page of owner in view v. A parent page whose last slot is freed
+ * merges back into its own level, recursively up to the huge page
+ * (explainer: reclaiming takes the same path in reverse).
+ * Errors: EINVAL (owner holds no page in v, e.g. a double free). */
+rimuru_status rimuru_view_free(rimuru_view* v, uint64_t owner);
+
+/* Copy the pool byte offsets of owner's pages in v, in allocation order, to
+ * out_offsets (capacity cap entries); *n_out receives the page count even
+ * when it exceeds cap (then nothing is copied and EINVAL is returned). An
+ * owner with no page yields *n_out = 0 and OK. */
+rimuru_status rimuru_view_pages(const rimuru_view* v, uint64_t owner, int64_t* out_offsets,
+                                uint64_t cap, uint64_t* n_out);
+
+/* Workload-aware adjuster mechanism (paper summary, abstract; explainer,
+ * paragraph on the adjuster): capacity moves between views by budget.
+ * A budget caps the bytes a view's owners may hold (pages * page_bytes);
+ * UINT64_MAX means no limit. Resident pages never move.
+ *   rimuru_view_set_budget: EBUSY if bytes is below what the owners hold.
+ *   rimuru_pool_transfer: moves bytes of budget from one view to another
+ *     view of the same pool; both must have a finite budget (EINVAL);
+ *     EBUSY if the source would drop below what its owners hold. */
+rimuru_status rimuru_view_set_budget(rimuru_view* v, uint64_t bytes);
+rimuru_status rimuru_pool_transfer(rimuru_pool* pool, rimuru_view* from, rimuru_view* to,
+                                   uint64_t bytes);
+/* Bytes held by the view's owners, and its budget (UINT64_MAX = none). */
+rimuru_status rimuru_view_usage(const rimuru_view* v, uint64_t* used_bytes,
+                                uint64_t* budget_bytes);
+
+typedef struct {
+  uint64_t huge_pages;        /* whole huge pages in the pool */
+  uint64_t huge_free;         /* huge pages not split for any view */
+  uint64_t bytes_per_kind[4]; /* bytes held by owners, per RIMURU_VIEW_* kind */
+  uint64_t bytes_free;        /* free huge pages + free slots of split pages */
+  uint64_t waste_bytes;       /* pool tail + split remainders */
+  uint64_t split_parents;     /* parent pages currently split, all views */
+} rimuru_pool_stats_t;
+/* bytes_per_kind summed + bytes_free + waste_bytes == pool_bytes. */
+rimuru_status rimuru_pool_stats(const rimuru_pool* pool, rimuru_pool_stats_t* out);
+
+/* Full internal consistency check (slow; for tests). EINVAL with a message
+ * naming the first broken invariant. */
+rimuru_status rimuru_pool_check(const rimuru_pool* pool);
+
+/* ------------------------------------------------------------------------ */
+/* Page-table-aware fused MoE                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Arguments of rimuru_fused_moe_paged. All pointers are device pointers
+ * unless stated; all arrays are row-major and densely packed.
+ *
+ * Expert weights live in the pool. Expert e owns three projections, in this
+ * order: w1 [H, I] (gate), w3 [H, I] (up), w2 [I, H] (down) (Table 1 of the
+ * paper summary gives the shapes; the gate/up/down roles are this library's
+ * reading). Byte f of projection p of expert e lives at
+ *     pool_base + pt[(e*3 + p)*P + f / page_bytes] * page_bytes + f % page_bytes.
+ */
+typedef struct {
+  int32_t T;           /* tokens, >= 0 (0 is a no-op) */
+  int32_t E;           /* experts, 1..512 */
+  int32_t k;           /* experts per token, 1..min(E, 32) */
+  int32_t H;           /* hidden size, a positive multiple of 64 */
+  int32_t I;           /* intermediate size, a positive multiple of 64 */
+  int32_t P;           /* pages per projection in pt; P*page_bytes >= H*I*es */
+  int32_t dtype;       /* RIMURU_BF16 or RIMURU_F32: x, weights and y share it */
+  int32_t renormalize; /* must be 1: the kept top-k weights sum to one */
+  const void* x;       /* [T, H] tokens */
+  const float* logits; /* [T, E] fp32 router logits; finite (precondition) */
+  const void* pool_base; /* pool start, 256-byte aligned */
+  const int32_t* pt;   /* [E][3][P] page indices in units of page_bytes; every
+                          entry an expert with routed tokens uses must lie in
+                          the pool (precondition, not checked per call) */
+  uint64_t page_bytes; /* expert-view page, a multiple of 128 */
+  void* y;             /* [T, H] output, dtype */
+  int32_t* topk_ids;   /* [T, k] out: expert ids in rank order */
+  float* topk_w;       /* [T, k] out: renormalised weights */
+  int32_t* sorted_ids; /* [sorted_len] out: routed slots t*k + j grouped by expert
+                          (ascending expert, ascending slot), each expert's
+                          segment padded with T*k to a multiple of block_m */
+  int32_t* expert_off; /* [E + 1] out: start of each expert's padded segment;
+                          expert_off[E] = total padded length */
+  void* workspace;     /* scratch, workspace_bytes from rimuru_moe_sizes,
+                          256-byte aligned; contents undefined on return */
+  uint64_t workspace_bytes;
+  void* const* stage_events; /* optional host array of hipEvent_t (NULL = none):
+                          n_stage_events == RIMURU_MOE_STAGES + 1; event i is
+                          recorded on the stream before stage i, the last one
+                          after the last stage */
+  int32_t n_stage_events;
+} rimuru_moe_args;
+
+/* Stages, in launch order: gating top-k, per-expert count, sort + tile align,
+ * gate/up GEMM with SiLU, down GEMM with routing weight, top-k combine. */
+#define RIMURU_MOE_STAGES 6
+
+/* Buffer sizes for a call with these shapes: sorted_len (entries of
+ * sorted_ids), workspace_bytes, and the tile height block_m the segments are
+ * padded to. Any output pointer may be NULL. The workspace does not depend
+ * on the size of the expert weights: the layer never copies them.
+ * Errors: EINVAL, EDTYPE. */
+rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+                               int32_t dtype, uint64_t* sorted_len,
+                               uint64_t* workspace_bytes, int32_t* block_m);
+
+/* Enqueue the fused MoE layer on hip_stream (a hipStream_t; NULL = the null
+ * stream) and return without synchronising. Arguments are validated on the
+ * host first; nothing is enqueued on error. Device faults from a broken
+ * precondition surface at the caller's next synchronisation.
+ * Errors: EINVAL, EDTYPE, EHIP (a launch or event record failed). */
+rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream);
+
+/* Host-side check that every entry of a host copy of pt (E*3*P entries)
+ * names a page inside a pool of pool_bytes bytes. ERANGE names the first bad
+ * entry. */
+rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int32_t P,
+                              uint64_t page_bytes, uint64_t pool_bytes);
+
+/* Load expert weights into their pages: copy src (device, [E][3][proj_bytes]
+ * contiguous) into the pool pages pt names, page by page, on hip_stream.
+ * This is how weights reach the pool (the reverse of the contiguous copy the
+ * layer avoids); it is not part of the layer. proj_bytes <= P*page_bytes,
+ * proj_bytes a multiple of 16, page_bytes a multiple of 128.
+ * Errors: EINVAL, EHIP. */
+rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt, int32_t E, int32_t P,
+                                   uint64_t page_bytes, const void* src, uint64_t proj_bytes,
+                                   void* hip_stream);
+
+/* Small event helpers so callers can time stages without linking HIP:
+ * create/destroy a timing-enabled hipEvent_t, and the elapsed milliseconds
+ * between two recorded events (synchronises on the second). */
+rimuru_status rimuru_event_create(void** ev);
+rimuru_status rimuru_event_destroy(void* ev);
+rimuru_status rimuru_event_record(void* ev, void* hip_stream);
+rimuru_status rimuru_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIMURU_H */

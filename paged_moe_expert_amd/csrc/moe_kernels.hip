@@ -1,0 +1,834 @@
+// Page-table-aware fused MoE for CDNA4 (gfx950).
+//
+// Rimuru paper summary (thelatestinai.com), abstract: a fused MoE kernel that
+// reads non-contiguous expert weights directly through the expert view's page
+// table, so no expert is ever copied into a contiguous buffer; Figure 11 names
+// it "Discrete FusedMoE". Explainer "Rimuru unifies serving memory"
+// (learnaivisually.com), paragraph on the two pieces that make the moving
+// fence usable: the kernel reads expert pages where they sit. Table 1 of the
+// summary gives the three projections per expert (w1, w3 [H, I], w2 [I, H]).
+//
+// Stages (one launch each, all on the caller's stream, no host sync):
+//   1 gating     one wavefront per token: top-k on raw logits, then softmax
+//                over the kept logits (the renormalised softmax weights)
+//   2 count      one workgroup per expert: routed slots per expert
+//   3 sort       one workgroup per expert: stable list of slots t*k+j,
+//                padded to the tile height, tile -> expert map
+//   4 gemm-up    grouped GEMM over sorted rows: h = SiLU(x w1) * (x w3),
+//                w1/w3 tiles fetched page by page
+//   5 gemm-down  grouped GEMM: y_slot[t*k+j] = w[t,j] * (h w2)
+//   6 combine    y[t] = sum_j y_slot[t*k+j], j in rank order
+//
+// Every 16-byte weight segment a lane loads gets its own page lookup
+// (page = offset / page_bytes by multiply-shift, then the page table); a
+// segment never straddles a page because pages are multiples of 128 bytes and
+// segments start on 16-byte boundaries. Results do not depend on where the
+// pages sit, so the paged and the contiguous layouts give identical bits.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rimuru.h"
+#include "rimuru_internal.h"
+
+namespace rimuru {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 512;
+
+// offset / page for offset < 2^31 by one 64-bit multiply and a shift
+// (Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994: m = 2^32 + floor(2^32 (2^l - d) / d) + 1, l = ceil
+// log2 d, q = (n m) >> (32 + l)).
+struct PageDiv {
+  uint64_t mul;
+  uint32_t shift;
+  uint32_t page;
+};
+
+__device__ __forceinline__ uint32_t page_index(uint32_t f, const PageDiv& d) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(f) * d.mul) >> d.shift);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+
+// ---------------------------------------------------------------- elements
+
+template <typename T>
+struct Elt;
+
+// bf16 stored as its 16-bit pattern.
+template <>
+struct Elt<uint16_t> {
+  static constexpr int ES = 2;
+  static constexpr int VEC = 8;  // elements per 16-byte segment
+  static constexpr int KI = 32;  // K of one MFMA (v_mfma_f32_16x16x32_bf16)
+  static constexpr int FE = 8;   // elements of one operand per lane
+  typedef u32x4 Frag;
+  static __device__ __forceinline__ Frag frag(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
+  static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f32(uint32_t bits) { return bf16_to_f32(bits); }
+  static __device__ __forceinline__ uint32_t from_f32(float v) { return f32_to_bf16(v); }
+  static __device__ __forceinline__ void put(uint16_t* p, float v) {
+    *p = static_cast<uint16_t>(f32_to_bf16(v));
+  }
+  // element c of a 16-byte segment
+  static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) {
+    return (s[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
+  }
+};
+
+template <>
+struct Elt<float> {
+  static constexpr int ES = 4;
+  static constexpr int VEC = 4;
+  static constexpr int KI = 4;   // v_mfma_f32_16x16x4_f32
+  static constexpr int FE = 1;
+  typedef float Frag;
+  static __device__ __forceinline__ Frag frag(const float* p) { return *p; }
+  static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f32(uint32_t bits) { return __uint_as_float(bits); }
+  static __device__ __forceinline__ uint32_t from_f32(float v) { return __float_as_uint(v); }
+  static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) { return s[c]; }
+};
+
+// ---------------------------------------------------------------- stage 1: gating
+
+// Total order on (logit, expert): larger logit first, then lower index;
+// -0 and +0 compare equal. Logits are finite (precondition).
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  uint32_t s = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(s) << 32) | (0xffffffffu - e);
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  uint32_t s = static_cast<uint32_t>(key >> 32);
+  uint32_t u = (s & 0x80000000u) ? (s & 0x7fffffffu) : ~s;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits, int T, int E,
+                                                int k, int32_t* __restrict__ ids,
+                                                float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + static_cast<int64_t>(t) * E;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    key[i] = (e < E) ? rank_key(row[e], static_cast<uint32_t>(e)) : 0ull;
+  }
+  uint32_t my_e = 0;
+  float my_l = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    uint32_t e = 0xffffffffu - static_cast<uint32_t>(best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (static_cast<uint32_t>(lane + 64 * i) == e) key[i] = 0ull;
+    if (lane == r) {
+      my_e = e;
+      my_l = key_logit(best);
+    }
+  }
+  const float m = __shfl(my_l, 0, 64);
+  const float ex = (lane < k) ? expf(my_l - m) : 0.0f;
+  const float s = wave_sum_f32(ex);
+  if (lane < k) {
+    ids[static_cast<int64_t>(t) * k + lane] = static_cast<int32_t>(my_e);
+    w[static_cast<int64_t>(t) * k + lane] = ex / s;
+  }
+}
+
+// ---------------------------------------------------------------- stage 2: count
+
+__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int TK,
+                                               int32_t* __restrict__ counts) {
+  __shared__ int part[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int f = threadIdx.x; f < TK; f += 256) c += (ids[f] == e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[e] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ---------------------------------------------------------------- stage 3: sort + align
+
+// Exclusive prefix of v over the 256 threads of the block; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sh[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += (i < wv) ? sh[i] : 0;
+    all += sh[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+constexpr int kSortChunk = 16;  // consecutive slots per thread per round
+
+__global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
+                                                    int BM, const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ sorted_ids,
+                                                    int32_t* __restrict__ expert_off,
+                                                    int32_t* __restrict__ tile_expert) {
+  __shared__ int sh[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  // start of this expert's padded segment, and the padded total
+  int before = 0, total = 0;
+  for (int e2 = tid; e2 < E; e2 += 256) {
+    int pc = (counts[e2] + BM - 1) / BM * BM;
+    total += pc;
+    before += (e2 < e) ? pc : 0;
+  }
+  int sum_before, sum_total;
+  block_excl_scan(before, &sum_before, sh);   // block sums of the per-thread partials
+  block_excl_scan(total, &sum_total, sh);
+  const int seg = sum_before;
+  const int cnt = counts[e];
+  if (tid == 0) {
+    expert_off[e] = seg;
+    if (e == 0) expert_off[E] = sum_total;
+  }
+  int running = 0;
+  for (int base = 0; base < TK; base += 256 * kSortChunk) {
+    const int f0 = base + tid * kSortChunk;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < kSortChunk; ++i) {
+      int f = f0 + i;
+      if (f < TK && ids[f] == e) mask |= 1u << i;
+    }
+    int chunk_total;
+    int pos = seg + running + block_excl_scan(__popc(mask), &chunk_total, sh);
+#pragma unroll
+    for (int i = 0; i < kSortChunk; ++i)
+      if (mask & (1u << i)) sorted_ids[pos++] = f0 + i;
+    running += chunk_total;
+  }
+  const int padded = (cnt + BM - 1) / BM * BM;
+  for (int i = cnt + tid; i < padded; i += 256) sorted_ids[seg + i] = TK;
+  for (int i = tid; i < padded / BM; i += 256) tile_expert[seg / BM + i] = e;
+}
+
+// ---------------------------------------------------------------- stages 4, 5: paged grouped GEMM
+
+struct GemmArgs {
+  const uint8_t* A;            // GEMM-up: x [T, H]; GEMM-down: h [sorted_len, I]
+  int64_t lda;                 // elements per A row
+  const int32_t* sorted_ids;
+  int kdiv;                    // GEMM-up: token = slot / kdiv
+  const uint8_t* pool;
+  const int32_t* pt;
+  int P;
+  PageDiv pd;
+  int K, N;                    // C[M, N] = A[M, K] B[K, N]
+  const int32_t* tile_expert;
+  const int32_t* expert_off;
+  int E;
+  uint8_t* C;                  // GEMM-up: h; GEMM-down: y_slot [T*k, H]
+  int64_t ldc;
+  const float* topk_w;
+  int TK;                      // number of routed slots; also the padding sentinel
+};
+
+// One workgroup computes a BM x BN tile of C (two tiles, w1 and w3, when
+// GATED). WM x WN wavefronts each own a (BM/WM) x (BN/WN) block of 16x16
+// MFMA tiles. K advances BK at a time through a double-buffered LDS stage:
+// A rows stored K-contiguous; weight tiles, which are N-contiguous in the
+// pool, are transposed in registers on their way into LDS so every MFMA
+// operand is one 16-byte LDS read per lane.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED>
+__global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
+  typedef Elt<T> X;
+  constexpr int NT = WM * WN * 64;
+  constexpr int VEC = X::VEC;
+  constexpr int NB = GATED ? 2 : 1;
+  constexpr int BKP = BK + VEC;                  // 16 bytes of row padding
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int A_SEGS = BM * BK / VEC;
+  constexpr int A_LOADS = (A_SEGS + NT - 1) / NT;
+  constexpr int RK = BK * BN / (VEC * NT);       // weight rows per thread per matrix
+  constexpr int CG = BN / VEC;                   // 16-byte column groups per weight row
+  static_assert(RK >= 1 && RK * VEC * NT == BK * BN, "weight tile must split evenly");
+  static_assert(BK % RK == 0 && WTM % 16 == 0 && WTN % 16 == 0 && BK % X::KI == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) T As[2][BM * BKP];
+  __shared__ __attribute__((aligned(16))) T Bs[2][NB][BN * BKP];
+
+  // ---- tile assignment: each XCD (dispatch round-robins over 8) takes one
+  // contiguous chunk of the live tiles, walked GM row-tiles at a time.
+  const int nN = a.N / BN;
+  const int n_tiles = a.expert_off[a.E] / BM;
+  const int L = n_tiles * nN;
+  const int chunk = (L + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  if (idx >= chunk) return;
+  const int logical = xcd * chunk + idx;
+  if (logical >= L) return;
+  const int gsz = GM * nN;
+  const int g = logical / gsz;
+  const int rr = logical - g * gsz;
+  const int m_first = g * GM;
+  const int gm = min(GM, n_tiles - m_first);
+  const int mt = m_first + rr % gm;
+  const int nt = rr / gm;
+  const int e = a.tile_expert[mt];
+  const int r0 = mt * BM;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / WN, wn = wv % WN;
+
+  // ---- A row sources for this tile
+  const T* a_src[A_LOADS];
+  int a_row[A_LOADS], a_kv[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    int s = tid + i * NT;
+    a_row[i] = s / (BK / VEC);
+    a_kv[i] = s % (BK / VEC);
+    a_src[i] = nullptr;
+    if (s < A_SEGS) {
+      int r = r0 + a_row[i];
+      if (a.kdiv > 0) {
+        int slot = a.sorted_ids[r];
+        if (slot < a.TK)
+          a_src[i] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(slot / a.kdiv) * a.lda;
+      } else {
+        a_src[i] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r) * a.lda;
+      }
+    }
+  }
+  // ---- weight segment of this thread: rows rb*RK .. +RK-1, columns cb*VEC .. +VEC-1
+  const int cb = tid % CG, rb = tid / CG;
+  const int32_t* pt_row[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) pt_row[b] = a.pt + static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P;
+
+  u32x4 a_reg[A_LOADS];
+  u32x4 b_reg[NB][RK];
+
+  auto load_stage = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      if (a_src[i] != nullptr)
+        a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK + a_kv[i] * VEC);
+      else
+        a_reg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < RK; ++j) {
+        uint32_t row = static_cast<uint32_t>(kt * BK + rb * RK + j);
+        uint32_t f = (row * static_cast<uint32_t>(a.N) + static_cast<uint32_t>(n0 + cb * VEC)) * X::ES;
+        uint32_t q = page_index(f, a.pd);
+        const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+        b_reg[b][j] = *reinterpret_cast<const u32x4*>(p);
+      }
+    }
+  };
+
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      if (tid + i * NT < A_SEGS)
+        *reinterpret_cast<u32x4*>(&As[buf][a_row[i] * BKP + a_kv[i] * VEC]) = a_reg[i];
+    }
+    // transpose: column c of the segment gets RK consecutive K values
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        T* dst = &Bs[buf][b][(cb * VEC + c) * BKP + rb * RK];
+        if constexpr (X::ES * RK == 2) {
+          *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(X::get(b_reg[b][0], c));
+        } else if constexpr (X::ES * RK == 4) {
+          uint32_t v = (X::ES == 2) ? (X::get(b_reg[b][0], c) | (X::get(b_reg[b][1], c) << 16))
+                                    : X::get(b_reg[b][0], c);
+          *reinterpret_cast<uint32_t*>(dst) = v;
+        } else if constexpr (X::ES * RK == 8) {
+          u32x2 v;
+          if constexpr (X::ES == 2) {
+            v[0] = X::get(b_reg[b][0], c) | (X::get(b_reg[b][1], c) << 16);
+            v[1] = X::get(b_reg[b][2], c) | (X::get(b_reg[b][3], c) << 16);
+          } else {
+            v[0] = X::get(b_reg[b][0], c);
+            v[1] = X::get(b_reg[b][1], c);
+          }
+          *reinterpret_cast<u32x2*>(dst) = v;
+        } else {
+          static_assert(X::ES * RK == 16, "unsupported weight rows per thread");
+          u32x4 v;
+          if constexpr (X::ES == 2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              v[j] = X::get(b_reg[b][2 * j], c) | (X::get(b_reg[b][2 * j + 1], c) << 16);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = X::get(b_reg[b][j], c);
+          }
+          *reinterpret_cast<u32x4*>(dst) = v;
+        }
+      }
+    }
+  };
+
+  f32x4 acc[NB][TM][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = a.K / BK;
+  const int fi = lane & 15, fq = lane >> 4;  // operand row/column and K group of this lane
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_stage(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / X::KI; ++kk) {
+      typename X::Frag af[TM], bfr[NB][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = X::frag(&As[buf][(wm * WTM + i * 16 + fi) * BKP + kk * X::KI + fq * X::FE]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[b][j] = X::frag(&Bs[buf][b][(wn * WTN + j * 16 + fi) * BKP + kk * X::KI + fq * X::FE]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[b][i][j] = X::mma(af[i], bfr[b][j], acc[b][i][j]);
+    }
+    if (kt + 1 < nk) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
+  T* C = reinterpret_cast<T*>(a.C);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = r0 + wm * WTM + i * 16 + 4 * fq + r;
+      if constexpr (GATED) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * WTN + j * 16 + fi;
+          float v = silu(acc[0][i][j][r]) * acc[1][i][j][r];
+          X::put(&C[static_cast<int64_t>(row) * a.ldc + col], v);
+        }
+      } else {
+        const int slot = a.sorted_ids[row];
+        if (slot < a.TK) {
+          const float wt = a.topk_w[slot];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + fi;
+            X::put(&C[static_cast<int64_t>(slot) * a.ldc + col], wt * acc[0][i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage 6: combine
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ yslot, int k, int H,
+                                                 T* __restrict__ y) {
+  typedef Elt<T> X;
+  constexpr int VEC = X::VEC;
+  const int t = blockIdx.x;
+  const int h0 = (blockIdx.y * 256 + threadIdx.x) * VEC;
+  if (h0 >= H) return;
+  float acc[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) acc[c] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    u32x4 s = *reinterpret_cast<const u32x4*>(yslot + (static_cast<int64_t>(t) * k + j) * H + h0);
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] += X::to_f32(X::get(s, c));
+  }
+  u32x4 o;
+  if constexpr (X::ES == 2) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = X::from_f32(acc[2 * c]) | (X::from_f32(acc[2 * c + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = X::from_f32(acc[c]);
+  }
+  *reinterpret_cast<u32x4*>(y + static_cast<int64_t>(t) * H + h0) = o;
+}
+
+// ---------------------------------------------------------------- weight loading
+
+__global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool,
+                                                     const int32_t* __restrict__ pt, int P,
+                                                     PageDiv pd, const uint8_t* __restrict__ src,
+                                                     uint64_t proj_bytes, uint64_t n_segs) {
+  for (uint64_t s = blockIdx.x * 256ull + threadIdx.x; s < n_segs; s += gridDim.x * 256ull) {
+    uint64_t byte = s * 16;
+    uint64_t proj = byte / proj_bytes;
+    uint32_t off = static_cast<uint32_t>(byte - proj * proj_bytes);
+    uint32_t q = page_index(off, pd);
+    uint8_t* dst = pool + static_cast<uint64_t>(pt[proj * P + q]) * pd.page + (off - q * pd.page);
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + byte);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+PageDiv make_div(uint32_t page) {
+  uint32_t l = 0;
+  while ((1ull << l) < page) ++l;
+  unsigned __int128 num = (static_cast<unsigned __int128>(1) << 32) * ((1ull << l) - page);
+  uint64_t m = static_cast<uint64_t>(num / page) + 1 + (1ull << 32);
+  return PageDiv{m, 32 + l, page};
+}
+
+// Tile height by expected rows per expert (T*k/E): few rows per expert is a
+// weight stream (decode), many rows is a dense grouped GEMM (prefill).
+enum PlanId { kPlan16 = 0, kPlan64 = 1, kPlan128 = 2 };
+struct Plan {
+  PlanId id;
+  int bm;
+};
+
+Plan choose_plan(int64_t T, int E, int k) {
+  int64_t tk = T * k;
+  if (tk <= 24ll * E) return {kPlan16, 16};
+  if (tk <= 160ll * E) return {kPlan64, 64};
+  return {kPlan128, 128};
+}
+
+struct Layout {
+  uint64_t tiles_max, sorted_len;
+  uint64_t off_counts, off_tiles, off_h, off_yslot, total;
+};
+
+Layout layout_for(int64_t T, int E, int k, int H, int I, int es, int bm) {
+  Layout l;
+  int64_t tk = T * k;
+  l.tiles_max = static_cast<uint64_t>(tk / bm + (tk < E ? tk : E));
+  l.sorted_len = l.tiles_max * bm;
+  l.off_counts = 0;
+  l.off_tiles = align_up(static_cast<uint64_t>(E) * 4);
+  l.off_h = l.off_tiles + align_up(l.tiles_max * 4);
+  l.off_yslot = l.off_h + align_up(l.sorted_len * static_cast<uint64_t>(I) * es);
+  l.total = l.off_yslot + align_up(static_cast<uint64_t>(tk) * H * es);
+  return l;
+}
+
+rimuru_status check_shapes(int64_t T, int E, int k, int H, int I, int dtype) {
+  if (dtype != RIMURU_BF16 && dtype != RIMURU_F32)
+    return rimuru_fail(RIMURU_EDTYPE, "dtype %d is neither RIMURU_BF16 nor RIMURU_F32", dtype);
+  if (T < 0) return rimuru_fail(RIMURU_EINVAL, "T = %lld is negative", (long long)T);
+  if (E < 1 || E > kMaxE) return rimuru_fail(RIMURU_EINVAL, "E = %d outside [1, %d]", E, kMaxE);
+  if (k < 1 || k > E || k > kMaxK)
+    return rimuru_fail(RIMURU_EINVAL, "k = %d outside [1, min(E, %d)]", k, kMaxK);
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0)
+    return rimuru_fail(RIMURU_EINVAL, "H = %d and I = %d must be positive multiples of 64", H, I);
+  if (T * k >= (1ll << 30)) return rimuru_fail(RIMURU_EINVAL, "T*k = %lld is too large", (long long)(T * k));
+  return RIMURU_OK;
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED>
+hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
+  uint64_t grid = (blocks + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_paged_gemm<T, BM, BN, BK, WM, WN, GM, GATED>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(WM * WN * 64), 0, st, g);
+  return hipGetLastError();
+}
+
+template <typename T, bool GATED>
+hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  switch (p.id) {
+    case kPlan16: return launch_gemm<T, 16, 64, 64, 1, 4, 1, GATED>(g, tiles_max, st);
+    case kPlan64: return launch_gemm<T, 64, 128, 32, 2, 2, 4, GATED>(g, tiles_max, st);
+    default: return launch_gemm<T, 128, 128, 32, 2, 2, 8, GATED>(g, tiles_max, st);
+  }
+}
+
+template <typename T>
+hipError_t launch_layer(const rimuru_moe_args* a, Plan p, const Layout& lay, hipStream_t st) {
+  const int T_ = a->T, E = a->E, k = a->k, H = a->H, I = a->I;
+  const int TK = T_ * k;
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.off_counts);
+  int32_t* tile_expert = reinterpret_cast<int32_t*>(ws + lay.off_tiles);
+  uint8_t* h = ws + lay.off_h;
+  uint8_t* yslot = ws + lay.off_yslot;
+  hipEvent_t* ev = a->stage_events ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->stage_events)) : nullptr;
+  hipError_t err;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+
+  if ((err = mark(0)) != hipSuccess) return err;
+  {
+    dim3 grid((T_ + 3) / 4);
+    int epl = (E + 63) / 64;
+    if (epl <= 1) hipLaunchKernelGGL(k_gating<1>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
+    else if (epl <= 2) hipLaunchKernelGGL(k_gating<2>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
+    else if (epl <= 4) hipLaunchKernelGGL(k_gating<4>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
+    else hipLaunchKernelGGL(k_gating<8>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if ((err = mark(1)) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, st, a->topk_ids, TK, counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = mark(2)) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_sort_align, dim3(E), dim3(256), 0, st, a->topk_ids, TK, E, p.bm, counts,
+                     a->sorted_ids, a->expert_off, tile_expert);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  GemmArgs g{};
+  g.sorted_ids = a->sorted_ids;
+  g.pool = static_cast<const uint8_t*>(a->pool_base);
+  g.pt = a->pt;
+  g.P = a->P;
+  g.pd = make_div(static_cast<uint32_t>(a->page_bytes));
+  g.tile_expert = tile_expert;
+  g.expert_off = a->expert_off;
+  g.E = E;
+  g.topk_w = a->topk_w;
+  g.TK = TK;
+
+  if ((err = mark(3)) != hipSuccess) return err;
+  g.A = static_cast<const uint8_t*>(a->x);
+  g.lda = H;
+  g.kdiv = k;
+  g.K = H;
+  g.N = I;
+  g.C = h;
+  g.ldc = I;
+  if ((err = launch_plan<T, true>(p, g, lay.tiles_max, st)) != hipSuccess) return err;
+
+  if ((err = mark(4)) != hipSuccess) return err;
+  g.A = h;
+  g.lda = I;
+  g.kdiv = 0;
+  g.K = I;
+  g.N = H;
+  g.C = yslot;
+  g.ldc = H;
+  if ((err = launch_plan<T, false>(p, g, lay.tiles_max, st)) != hipSuccess) return err;
+
+  if ((err = mark(5)) != hipSuccess) return err;
+  {
+    constexpr int VEC = Elt<T>::VEC;
+    dim3 grid(T_, (H + 256 * VEC - 1) / (256 * VEC));
+    hipLaunchKernelGGL(k_combine<T>, grid, dim3(256), 0, st, reinterpret_cast<const T*>(yslot), k, H,
+                       static_cast<T*>(a->y));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return mark(6);
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+}  // namespace rimuru
+
+using namespace rimuru;
+
+extern "C" rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+                                          int32_t dtype, uint64_t* sorted_len,
+                                          uint64_t* workspace_bytes, int32_t* block_m) {
+  rimuru_status s = check_shapes(T, E, k, H, I, dtype);
+  if (s != RIMURU_OK) return s;
+  Plan p = choose_plan(T, E, k);
+  Layout l = layout_for(T, E, k, H, I, dtype == RIMURU_BF16 ? 2 : 4, p.bm);
+  if (sorted_len) *sorted_len = l.sorted_len;
+  if (workspace_bytes) *workspace_bytes = l.total;
+  if (block_m) *block_m = p.bm;
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream) {
+  if (a == nullptr) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged: args is NULL");
+  rimuru_status s = check_shapes(a->T, a->E, a->k, a->H, a->I, a->dtype);
+  if (s != RIMURU_OK) return s;
+  if (a->renormalize != 1)
+    return rimuru_fail(RIMURU_EINVAL, "renormalize must be 1 (the kept top-k weights sum to one)");
+  if (a->T == 0) return RIMURU_OK;
+  const int es = a->dtype == RIMURU_BF16 ? 2 : 4;
+  const uint64_t proj = static_cast<uint64_t>(a->H) * a->I * es;
+  if (a->page_bytes == 0 || a->page_bytes % 128 != 0)
+    return rimuru_fail(RIMURU_EINVAL, "page_bytes %llu is not a positive multiple of 128",
+                       (unsigned long long)a->page_bytes);
+  if (a->P < 1 || static_cast<uint64_t>(a->P) * a->page_bytes < proj)
+    return rimuru_fail(RIMURU_EINVAL, "P = %d pages of %llu bytes cannot hold a %llu-byte projection",
+                       a->P, (unsigned long long)a->page_bytes, (unsigned long long)proj);
+  if (static_cast<uint64_t>(a->P) * a->page_bytes >= (1ull << 31))
+    return rimuru_fail(RIMURU_EINVAL, "a projection's pages must span less than 2 GiB");
+  if (!a->x || !a->logits || !a->pool_base || !a->pt || !a->y || !a->topk_ids || !a->topk_w ||
+      !a->sorted_ids || !a->expert_off || !a->workspace)
+    return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged: a required pointer is NULL");
+  if (!aligned(a->pool_base, 256) || !aligned(a->workspace, 256) || !aligned(a->x, 16) || !aligned(a->y, 16))
+    return rimuru_fail(RIMURU_EINVAL, "pool_base/workspace need 256-byte and x/y 16-byte alignment");
+  Plan p = choose_plan(a->T, a->E, a->k);
+  Layout lay = layout_for(a->T, a->E, a->k, a->H, a->I, es, p.bm);
+  if (a->workspace_bytes < lay.total)
+    return rimuru_fail(RIMURU_EINVAL, "workspace of %llu bytes is below the %llu needed",
+                       (unsigned long long)a->workspace_bytes, (unsigned long long)lay.total);
+  if ((a->stage_events == nullptr) != (a->n_stage_events == 0) ||
+      (a->stage_events && a->n_stage_events != RIMURU_MOE_STAGES + 1))
+    return rimuru_fail(RIMURU_EINVAL, "stage_events needs exactly %d events", RIMURU_MOE_STAGES + 1);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t err = (a->dtype == RIMURU_BF16) ? launch_layer<uint16_t>(a, p, lay, st)
+                                             : launch_layer<float>(a, p, lay, st);
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "launch failed: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int32_t P,
+                                         uint64_t page_bytes, uint64_t pool_bytes) {
+  if (pt_host == nullptr || E < 1 || P < 1 || page_bytes == 0)
+    return rimuru_fail(RIMURU_EINVAL, "pt_check: bad argument");
+  const uint64_t n = static_cast<uint64_t>(E) * 3 * P;
+  for (uint64_t i = 0; i < n; ++i) {
+    if (pt_host[i] < 0 || (static_cast<uint64_t>(pt_host[i]) + 1) * page_bytes > pool_bytes)
+      return rimuru_fail(RIMURU_ERANGE, "pt entry %llu (expert %llu, projection %llu, page %llu) = %d "
+                         "lies outside the pool", (unsigned long long)i,
+                         (unsigned long long)(i / (3ull * P)), (unsigned long long)(i / P % 3),
+                         (unsigned long long)(i % P), pt_host[i]);
+  }
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt, int32_t E, int32_t P,
+                                              uint64_t page_bytes, const void* src,
+                                              uint64_t proj_bytes, void* hip_stream) {
+  if (!pool_base || !pt || !src || E < 1 || P < 1)
+    return rimuru_fail(RIMURU_EINVAL, "experts_store: bad argument");
+  if (page_bytes == 0 || page_bytes % 128 != 0 || proj_bytes == 0 || proj_bytes % 16 != 0 ||
+      proj_bytes > static_cast<uint64_t>(P) * page_bytes ||
+      static_cast<uint64_t>(P) * page_bytes >= (1ull << 31))
+    return rimuru_fail(RIMURU_EINVAL, "experts_store: page %llu / projection %llu bytes / P %d do not fit",
+                       (unsigned long long)page_bytes, (unsigned long long)proj_bytes, P);
+  if (!aligned(pool_base, 256) || !aligned(src, 16))
+    return rimuru_fail(RIMURU_EINVAL, "experts_store: pool_base needs 256-byte, src 16-byte alignment");
+  uint64_t n_segs = static_cast<uint64_t>(E) * 3 * proj_bytes / 16;
+  uint64_t blocks = (n_segs + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_store_pages, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(hip_stream), static_cast<uint8_t*>(pool_base), pt, P,
+                     make_div(static_cast<uint32_t>(page_bytes)), static_cast<const uint8_t*>(src),
+                     proj_bytes, n_segs);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "experts_store: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_event_create(void** ev) {
+  if (!ev) return rimuru_fail(RIMURU_EINVAL, "event_create: NULL");
+  hipEvent_t e;
+  hipError_t err = hipEventCreate(&e);
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "hipEventCreate: %s", hipGetErrorString(err));
+  *ev = e;
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_event_destroy(void* ev) {
+  if (!ev) return RIMURU_OK;
+  hipError_t err = hipEventDestroy(static_cast<hipEvent_t>(ev));
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "hipEventDestroy: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_event_record(void* ev, void* hip_stream) {
+  hipError_t err = hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "hipEventRecord: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}
+
+extern "C" rimuru_status rimuru_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return rimuru_fail(RIMURU_EINVAL, "event_elapsed_ms: NULL");
+  hipError_t err = hipEventSynchronize(static_cast<hipEvent_t>(stop));
+  if (err == hipSuccess) err = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "event timing: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}

@@ -1,0 +1,224 @@
+"""Python binding of librimuru.so, one function per C entry point (the C
+name without its ``rimuru_`` prefix). Arguments are marshalled and statuses
+turned into RimuruError; all work happens in the library. Device buffers are
+torch tensors, streams are torch streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, MoeArgs, OK,  # noqa: F401
+                   PoolStats, RimuruError, check, lib)
+
+
+# ----------------------------------------------------------------- pool and views
+
+class Pool:
+    """Host state of one shared page pool (owns its views)."""
+
+    def __init__(self, handle: int, pool_bytes: int, huge_bytes: int):
+        self.handle = handle
+        self.pool_bytes = pool_bytes
+        self.huge_bytes = huge_bytes
+        self.views = []
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib().rimuru_pool_destroy(self.handle)
+            self.handle = None
+
+
+class View:
+    def __init__(self, pool: Pool, handle: int, kind: int, page_bytes: int):
+        self.pool = pool              # keeps the pool (which owns the view) alive
+        self.handle = handle
+        self.kind = kind
+        self.page_bytes = page_bytes
+
+
+def pool_create(pool_bytes: int, huge_page_bytes: int) -> Pool:
+    h = C.c_void_p()
+    check(lib().rimuru_pool_create(pool_bytes, huge_page_bytes, C.byref(h)), "pool_create")
+    return Pool(h.value, pool_bytes, huge_page_bytes)
+
+
+def view_map(pool: Pool, kind: int, page_bytes: int, parent: View | None = None) -> View:
+    h = C.c_void_p()
+    check(lib().rimuru_view_map(pool.handle, kind, page_bytes,
+                                parent.handle if parent is not None else None, C.byref(h)),
+          "view_map")
+    v = View(pool, h.value, kind, page_bytes)
+    pool.views.append(v)
+    return v
+
+
+def view_alloc_status(v: View, owner: int, n_pages: int):
+    """(status, offsets) without raising: ENOMEM is an ordinary outcome."""
+    out = np.zeros(max(n_pages, 1), dtype=np.int64)
+    st = lib().rimuru_view_alloc(v.handle, owner, n_pages, out.ctypes.data)
+    return st, (out[:n_pages] if st == OK else out[:0])
+
+
+def view_alloc(v: View, owner: int, n_pages: int) -> np.ndarray:
+    st, offs = view_alloc_status(v, owner, n_pages)
+    check(st, "view_alloc")
+    return offs
+
+
+def view_free_status(v: View, owner: int) -> int:
+    return lib().rimuru_view_free(v.handle, owner)
+
+
+def view_free(v: View, owner: int) -> None:
+    check(view_free_status(v, owner), "view_free")
+
+
+def view_pages(v: View, owner: int) -> np.ndarray:
+    n = C.c_uint64()
+    lib().rimuru_view_pages(v.handle, owner, None, 0, C.byref(n))   # count only
+    out = np.zeros(max(n.value, 1), dtype=np.int64)
+    check(lib().rimuru_view_pages(v.handle, owner, out.ctypes.data, n.value, C.byref(n)), "view_pages")
+    return out[:n.value]
+
+
+def view_set_budget(v: View, nbytes: int | None) -> int:
+    return lib().rimuru_view_set_budget(v.handle, NO_BUDGET if nbytes is None else nbytes)
+
+
+def pool_transfer(pool: Pool, src: View, dst: View, nbytes: int) -> int:
+    return lib().rimuru_pool_transfer(pool.handle, src.handle, dst.handle, nbytes)
+
+
+def view_usage(v: View):
+    used, budget = C.c_uint64(), C.c_uint64()
+    check(lib().rimuru_view_usage(v.handle, C.byref(used), C.byref(budget)), "view_usage")
+    return used.value, (None if budget.value == NO_BUDGET else budget.value)
+
+
+def pool_stats(pool: Pool) -> dict:
+    s = PoolStats()
+    check(lib().rimuru_pool_stats(pool.handle, C.byref(s)), "pool_stats")
+    return {"huge_pages": s.huge_pages, "huge_free": s.huge_free,
+            "bytes_per_kind": list(s.bytes_per_kind), "bytes_free": s.bytes_free,
+            "waste_bytes": s.waste_bytes, "split_parents": s.split_parents}
+
+
+def pool_check(pool: Pool) -> None:
+    check(lib().rimuru_pool_check(pool.handle), "pool_check")
+
+
+def pt_check(pt: np.ndarray, page_bytes: int, pool_bytes: int) -> None:
+    pt = np.ascontiguousarray(pt, dtype=np.int32)
+    E, three, P = pt.shape
+    check(lib().rimuru_pt_check(pt.ctypes.data, E, P, page_bytes, pool_bytes), "pt_check")
+
+
+# ----------------------------------------------------------------- fused MoE
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise RimuruError(-4, "fused_moe_paged", f"unsupported dtype {t.dtype}")
+
+
+def moe_sizes(T: int, E: int, k: int, H: int, I: int, dtype: int):
+    """(sorted_len, workspace_bytes, block_m)."""
+    sl, ws, bm = C.c_uint64(), C.c_uint64(), C.c_int32()
+    check(lib().rimuru_moe_sizes(T, E, k, H, I, dtype, C.byref(sl), C.byref(ws), C.byref(bm)),
+          "moe_sizes")
+    return sl.value, ws.value, bm.value
+
+
+class MoeBuffers:
+    """Outputs and workspace for one shape; reuse them across calls."""
+
+    def __init__(self, T, E, k, H, I, dtype, device="cuda"):
+        import torch
+        tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+        sl, ws, bm = moe_sizes(T, E, k, H, I, dtype)
+        self.shape = (T, E, k, H, I, dtype)
+        self.block_m = bm
+        self.y = torch.empty((T, H), dtype=tdt, device=device)
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.sorted_ids = torch.empty(max(sl, 1), dtype=torch.int32, device=device)
+        self.expert_off = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+
+def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
+                    bufs: MoeBuffers | None = None, stream=None, stage_events=None) -> MoeBuffers:
+    """Enqueue the fused MoE layer on the current (or given) torch stream.
+
+    x [T, H] bf16/fp32, logits [T, E] fp32, pool uint8 device tensor,
+    pt int32 [E, 3, P] device tensor, I the intermediate size. Returns the
+    buffers holding y, topk_ids, topk_w, sorted_ids and expert_off. Does not
+    synchronise.
+    """
+    import torch
+    T, H = x.shape
+    E = logits.shape[1]
+    P = pt.shape[2]
+    dt = _dtype_code(x)
+    if bufs is None:
+        bufs = MoeBuffers(T, E, k, H, I, dt, device=x.device)
+    a = MoeArgs()
+    a.T, a.E, a.k, a.H, a.I, a.P, a.dtype, a.renormalize = T, E, k, H, I, P, dt, 1
+    a.x, a.logits, a.pool_base, a.pt = x.data_ptr(), logits.data_ptr(), pool.data_ptr(), pt.data_ptr()
+    a.page_bytes = page_bytes
+    a.y, a.topk_ids, a.topk_w = bufs.y.data_ptr(), bufs.topk_ids.data_ptr(), bufs.topk_w.data_ptr()
+    a.sorted_ids, a.expert_off = bufs.sorted_ids.data_ptr(), bufs.expert_off.data_ptr()
+    a.workspace, a.workspace_bytes = bufs.workspace.data_ptr(), bufs.workspace.numel()
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (C.c_void_p * len(stage_events))(*stage_events)
+        a.stage_events = C.cast(ev_arr, C.c_void_p)
+        a.n_stage_events = len(stage_events)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    check(lib().rimuru_fused_moe_paged(C.byref(a), s.cuda_stream), "fused_moe_paged")
+    return bufs
+
+
+def fused_moe_paged_raw(args: MoeArgs, stream_handle: int) -> int:
+    """Direct entry for callers that fill MoeArgs themselves; returns the status."""
+    return lib().rimuru_fused_moe_paged(C.byref(args), stream_handle)
+
+
+def experts_store(pool, pt, weights, page_bytes: int, stream=None) -> None:
+    """Copy contiguous projections weights [E, 3, proj_bytes] (device, uint8 view
+    or any dtype) into the pool pages pt names."""
+    import torch
+    E, three, P = pt.shape
+    proj_bytes = weights[0, 0].numel() * weights.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(pool.device)
+    check(lib().rimuru_experts_store(pool.data_ptr(), pt.data_ptr(), E, P, page_bytes,
+                                     weights.data_ptr(), proj_bytes, s.cuda_stream), "experts_store")
+
+
+# ----------------------------------------------------------------- timing helpers
+
+def event_create() -> int:
+    h = C.c_void_p()
+    check(lib().rimuru_event_create(C.byref(h)), "event_create")
+    return h.value
+
+
+def event_destroy(ev: int) -> None:
+    check(lib().rimuru_event_destroy(ev), "event_destroy")
+
+
+def event_record(ev: int, stream=None) -> None:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    check(lib().rimuru_event_record(ev, s.cuda_stream), "event_record")
+
+
+def event_elapsed_ms(a: int, b: int) -> float:
+    ms = C.c_float()
+    check(lib().rimuru_event_elapsed_ms(a, b, C.byref(ms)), "event_elapsed_ms")
+    return ms.value

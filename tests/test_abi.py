@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every entry point include/rimuru.h declares,
+and validates arguments on the host (no GPU needed for any of these)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from paged_moe_expert_amd import _lib
+from paged_moe_expert_amd import rimuru as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rimuru.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rimuru_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    L = _lib.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding declares a prototype for each
+    assert set(names) <= set(_lib._PROTOS), set(names) - set(_lib._PROTOS)
+
+
+def test_abi_version_and_error_text():
+    L = _lib.lib()
+    assert L.rimuru_abi_version() == 1
+    assert L.rimuru_pool_create(100, 0, C.byref(C.c_void_p())) == _lib.EINVAL
+    assert b"huge page" in L.rimuru_last_error()
+
+
+def test_moe_sizes_and_plans():
+    sl, ws, bm = R.moe_sizes(64, 128, 8, 2048, 768, R.BF16)
+    assert bm == 16 and sl % bm == 0 and sl >= 64 * 8
+    # tiles bound: floor(T*k/bm) + min(E, T*k)
+    assert sl == (512 // 16 + 128) * 16
+    # the workspace never scales with expert weight bytes: only with tokens
+    assert ws < 16 * 2 ** 20
+    sl4, ws4, bm4 = R.moe_sizes(8192, 128, 8, 2048, 768, R.BF16)
+    assert bm4 == 128
+    _, _, bm3 = R.moe_sizes(2048, 256, 8, 2048, 512, R.BF16)
+    assert bm3 == 64
+    sl1, _, bm1 = R.moe_sizes(1, 128, 8, 2048, 768, R.BF16)
+    assert bm1 == 16 and sl1 == 8 * 16
+    with pytest.raises(_lib.RimuruError) as e:
+        R.moe_sizes(4, 8, 9, 128, 64, R.F32)
+    assert e.value.status == _lib.EINVAL
+    with pytest.raises(_lib.RimuruError) as e:
+        R.moe_sizes(4, 8, 2, 128, 64, 7)
+    assert e.value.status == _lib.EDTYPE
+    with pytest.raises(_lib.RimuruError):
+        R.moe_sizes(4, 8, 2, 100, 64, R.F32)          # H not a multiple of 64
+    with pytest.raises(_lib.RimuruError):
+        R.moe_sizes(4, 600, 2, 128, 64, R.F32)        # E above 512
+
+
+def _args(**over):
+    a = _lib.MoeArgs()
+    a.T, a.E, a.k, a.H, a.I, a.P, a.dtype, a.renormalize = 16, 8, 2, 128, 64, 8, R.F32, 1
+    a.page_bytes = 4096
+    for name in ("x", "logits", "pool_base", "pt", "y", "topk_ids", "topk_w", "sorted_ids",
+                 "expert_off", "workspace"):
+        setattr(a, name, 1 << 20)                       # never dereferenced: validation fails first
+    a.workspace_bytes = 1 << 30
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=0), _lib.EINVAL), (dict(k=9), _lib.EINVAL), (dict(E=0), _lib.EINVAL),
+    (dict(H=96), _lib.EINVAL), (dict(dtype=3), _lib.EDTYPE), (dict(renormalize=0), _lib.EINVAL),
+    (dict(page_bytes=100), _lib.EINVAL), (dict(P=7), _lib.EINVAL), (dict(x=0), _lib.EINVAL),
+    (dict(pool_base=(1 << 20) + 16), _lib.EINVAL), (dict(workspace_bytes=100), _lib.EINVAL),
+    (dict(n_stage_events=3), _lib.EINVAL), (dict(T=-1), _lib.EINVAL),
+])
+def test_fused_moe_rejects_bad_arguments_without_launching(over, status):
+    assert R.fused_moe_paged_raw(_args(**over), 0) == status
+
+
+def test_zero_tokens_is_a_noop():
+    a = _args(T=0, x=0, y=0, logits=0)
+    assert R.fused_moe_paged_raw(a, 0) == _lib.OK
+
+
+def test_pt_check_ranges():
+    pt = np.arange(8 * 3 * 4, dtype=np.int32).reshape(8, 3, 4)
+    R.pt_check(pt, 4096, 96 * 4096)
+    pt[5, 1, 2] = 96
+    with pytest.raises(_lib.RimuruError) as e:
+        R.pt_check(pt, 4096, 96 * 4096)
+    assert e.value.status == _lib.ERANGE and "expert 5, projection 1, page 2" in str(e.value)
+    pt[5, 1, 2] = -1
+    with pytest.raises(_lib.RimuruError):
+        R.pt_check(pt, 4096, 96 * 4096)
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "paged_moe_expert_amd")
+    for dp, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dp, f)).read()
+                assert "oracle" not in re.sub(r"#.*|//.*", "", txt).lower().replace("oracle/", ""), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            txt = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "paged_moe_expert_amd" not in txt and "rimuru" not in txt.replace("Rimuru", ""), f

@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars: top-k ids and per-expert lists bit-exact; weights within 2e-6
+(relative) and summing to one within 1e-6; y within a row-wise max-norm
+relative error of 1e-2 for bf16 and 1e-4 for fp32; paged and contiguous
+layouts bitwise equal; repeated runs bitwise equal.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from moe_inputs import CONFIGS, gen
+from moe_inputs.configs import CFG1, KIB
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+if torch.cuda.is_available():
+    from gpu_common import (Case, check_routing, contiguous_pool, decode_dev, paged_pool, rel_err,
+                            run, say, to_dev_bits, weights_dev)
+    from oracle.moe import moe_forward
+    from paged_moe_expert_amd import rimuru as R
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+# ---------------------------------------------------------------- custom shapes
+
+def _custom(name, E, k, H, I, T, dtype, page, bias=None, seed=0):
+    """A shape outside the registry, on a seeded random page permutation."""
+    cfg = replace(CFG1, cid=100 + seed, name=name, E=E, k=k, H=H, I=I, T=T, dtype=dtype,
+                  page_bytes=page, logits="normal")
+    es = cfg.es
+    P = -(-H * I * es // page)
+    n_pages = E * 3 * P + 7
+    r = np.random.default_rng(1000 + seed)
+    pt = r.permutation(n_pages)[:E * 3 * P].astype(np.int32).reshape(E, 3, P)
+    wb = gen.all_weight_bits(cfg)
+    xb = gen.x_bits(cfg, T)
+    lg = gen.logits(cfg, T)
+    if bias is not None:
+        lg = (lg + np.asarray(bias, dtype=np.float32)[None, :E]).astype(np.float32)
+    return cfg, P, n_pages, pt, wb, xb, lg
+
+
+def _ref_pool(n_pages, page, pt, wb, P):
+    pool = np.zeros(n_pages * page, dtype=np.uint8)
+    raw = wb.view(np.uint8).reshape(wb.shape[0], 3, -1)
+    nbytes = raw.shape[2]
+    for e in range(pt.shape[0]):
+        for p in range(3):
+            for q in range(P):
+                lo, hi = q * page, min((q + 1) * page, nbytes)
+                a = int(pt[e, p, q]) * page
+                pool[a:a + hi - lo] = raw[e, p, lo:hi]
+    return pool
+
+
+def _padded_weights(wb, P, page):
+    # weights tensor padded to P*page bytes per projection for the store call
+    es = wb.dtype.itemsize
+    E = wb.shape[0]
+    padded = np.zeros((E, 3, P * page // es), dtype=wb.dtype)
+    padded[:, :, :wb.shape[2]] = wb
+    return padded
+
+
+CUSTOM = [
+    # name, E, k, H, I, T, dtype, page, bias
+    ("bf16-decode-tiles", 16, 4, 256, 128, 40, "bf16", 4 * KIB, None),
+    ("bf16-mid-tiles", 16, 4, 256, 128, 300, "bf16", 4 * KIB, None),
+    ("bf16-mid-odd-page", 16, 4, 256, 128, 300, "bf16", 12 * KIB, None),
+    ("bf16-big-tiles", 16, 4, 256, 128, 1000, "bf16", 4 * KIB, None),
+    ("bf16-big-skewed", 16, 4, 256, 128, 1000, "bf16", 8 * KIB, [4, 3, 2.5, 2] + [0] * 10 + [-50, -50]),
+    ("f32-mid-tiles", 8, 2, 128, 64, 500, "f32", 4 * KIB, None),
+    ("f32-big-tiles", 8, 2, 128, 64, 1500, "f32", 4 * KIB, None),
+    ("bf16-k1", 4, 1, 128, 64, 33, "bf16", 4 * KIB, None),
+    ("bf16-k-equals-E", 8, 8, 128, 192, 19, "bf16", 4 * KIB, None),
+    ("bf16-one-expert", 1, 1, 192, 64, 50, "bf16", 4 * KIB, None),
+    ("bf16-128B-pages", 4, 2, 64, 64, 21, "bf16", 128, None),
+    ("bf16-one-token", 16, 4, 256, 128, 1, "bf16", 4 * KIB, None),
+]
+
+
+@pytest.mark.parametrize("spec", CUSTOM, ids=[c[0] for c in CUSTOM])
+def test_custom_shapes_against_oracle(spec):
+    name, E, k, H, I, T, dtype, page, bias = spec
+    say(f"[custom] {name}: E={E} k={k} H={H} I={I} T={T} {dtype} page={page}")
+    cfg, P, n_pages, pt, wb, xb, lg = _custom(name, E, k, H, I, T, dtype, page, bias,
+                                               seed=CUSTOM.index(spec))
+    wdev = weights_dev(_padded_weights(wb, P, page))
+    pool, ptd = paged_pool(n_pages * page, pt, wdev, page)
+    x = to_dev_bits(xb, dtype)
+    lgd = torch.from_numpy(lg).cuda()
+    bufs = R.fused_moe_paged(x, lgd, pool, ptd, page, k, I)
+    torch.cuda.synchronize()
+    ref = moe_forward(xb, lg, _ref_pool(n_pages, page, pt, wb, P), pt, page, E=E, k=k, H=H, I=I,
+                      dtype=dtype)
+    check_routing(bufs, ref, T, k, E, bufs.block_m)
+    y = decode_dev(bufs.y)
+    assert np.isfinite(y).all()
+    err = rel_err(y, ref["y"])
+    say(f"[custom] {name}: block_m={bufs.block_m} rel_err={err:.3e}")
+    assert err <= TOL[dtype]
+    # paged == contiguous, bitwise
+    cpool = wdev.view(torch.uint8).reshape(-1)
+    cpt = torch.arange(E * 3 * P, dtype=torch.int32, device="cuda").reshape(E, 3, P)
+    b2 = R.fused_moe_paged(x, lgd, cpool, cpt, page, k, I)
+    torch.cuda.synchronize()
+    assert torch.equal(b2.y, bufs.y)
+
+
+# ---------------------------------------------------------------- registry configs
+
+@pytest.fixture(scope="module")
+def tiny():
+    return Case(CONFIGS[1])
+
+
+def test_tiny_fp32_full_parity(tiny):
+    say("[cfg1] tiny fp32 layer, seeded scatter over a 256-page pool")
+    c = tiny
+    assert np.array_equal(c.pt, c.pt_ref)
+    bufs = c.run()
+    ref = c.oracle()
+    check_routing(bufs, ref, c.T, c.cfg.k, c.cfg.E, bufs.block_m)
+    err = rel_err(decode_dev(bufs.y), ref["y"])
+    say(f"[cfg1] rel_err={err:.3e}")
+    assert err <= TOL["f32"]
+
+
+def test_tiny_paged_equals_contiguous_and_repeats(tiny):
+    c = tiny
+    a = c.run()
+    ya = a.y.clone()
+    b = c.run()
+    assert torch.equal(b.y, ya)                       # run to run
+    pool, ptd = contiguous_pool(c.cfg, c.wdev)
+    cc = c.run(pool=pool, ptd=ptd)
+    assert torch.equal(cc.y, ya)                      # paged == contiguous
+
+
+def test_tiny_token_permutation_equivariance(tiny):
+    c = tiny
+    base = c.run().y.clone()
+    perm = torch.randperm(c.T, generator=torch.Generator().manual_seed(3)).cuda()
+    out = R.fused_moe_paged(c.x[perm].contiguous(), c.lgd[perm].contiguous(), c.pool, c.ptd,
+                            c.cfg.page_bytes, c.cfg.k, c.cfg.I)
+    torch.cuda.synchronize()
+    assert torch.equal(out.y, base[perm])
+
+
+def test_poisoned_idle_expert_pages_never_reach_output(tiny):
+    c = tiny
+    lg = c.lg.copy()
+    lg[:, 6:] = -1e30                                  # experts 6, 7 get no tokens
+    lgd = torch.from_numpy(lg).cuda()
+    out0 = R.fused_moe_paged(c.x, lgd, c.pool, c.ptd, c.cfg.page_bytes, c.cfg.k, c.cfg.I)
+    torch.cuda.synchronize()
+    y0 = out0.y.clone()
+    pool = c.pool.clone()
+    pv = pool.view(torch.int32)
+    P, page = c.cfg.P, c.cfg.page_bytes
+    for e in (6, 7):
+        for p in range(3):
+            for q in range(P):
+                a = int(c.pt[e, p, q]) * page // 4
+                pv[a:a + page // 4] = 0x7FC07FC0
+    out1 = R.fused_moe_paged(c.x, lgd, pool, c.ptd, page, c.cfg.k, c.cfg.I)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out1.y).all()
+    assert torch.equal(out1.y, y0)
+
+
+def _sample(T, n, seed=0):
+    r = np.random.default_rng(seed)
+    return np.sort(r.choice(T, size=min(n, T), replace=False))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid,n_sample", [(2, 64), (3, 24), (4, 24)])
+def test_full_size_configs(cid, n_sample):
+    cfg = CONFIGS[cid]
+    say(f"[cfg{cid}] {cfg.name}: T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} page={cfg.page_bytes}")
+    c = Case(cfg)
+    assert np.array_equal(c.pt, c.pt_ref)
+    bufs = c.run()
+    y = decode_dev(bufs.y)
+    assert np.isfinite(y).all()
+    toks = _sample(c.T, n_sample, cid)
+    ref = c.oracle(tokens=toks)
+    check_routing(bufs, ref, c.T, cfg.k, cfg.E, bufs.block_m)
+    err = rel_err(y[toks], ref["y"])
+    say(f"[cfg{cid}] block_m={bufs.block_m} sampled rel_err={err:.3e} over {len(toks)} tokens")
+    assert err <= TOL[cfg.dtype]
+    y0 = bufs.y.clone()
+    pool, ptd = contiguous_pool(cfg, c.wdev)
+    cc = c.run(pool=pool, ptd=ptd)
+    assert torch.equal(cc.y, y0), "paged and contiguous layouts differ"
+    again = c.run()
+    assert torch.equal(again.y, y0), "run-to-run difference"
+
+
+@pytest.mark.timeout(900)
+def test_decode_sweep_under_adjuster_steps():
+    cfg = CONFIGS[5]
+    base = Case(cfg, T=1)
+    dl, rl = base.dev_layout, base.ref_layout
+    dl.init_budgets()
+    rl.init_budgets()
+    for B in cfg.batches:
+        say(f"[cfg5] batch {B}")
+        xb, lg = gen.x_bits(cfg, B), gen.logits(cfg, B)
+        x, lgd = to_dev_bits(xb, cfg.dtype), torch.from_numpy(lg).cuda()
+        bufs = R.MoeBuffers(B, cfg.E, cfg.k, cfg.H, cfg.I, R.BF16)
+        out = run(cfg, x, lgd, base.pool, base.ptd, bufs)
+        y0 = out.y.clone()
+        toks = _sample(B, 16, B)
+        ref = moe_forward(xb, lg, base.ref_pool(), base.pt_ref, cfg.page_bytes, E=cfg.E, k=cfg.k,
+                          H=cfg.H, I=cfg.I, dtype=cfg.dtype, tokens=toks)
+        check_routing(out, ref, B, cfg.k, cfg.E, out.block_m)
+        err = rel_err(decode_dev(out.y)[toks], ref["y"])
+        say(f"[cfg5] B={B} rel_err={err:.3e}")
+        assert err <= TOL["bf16"]
+        s1, s2 = gen.adjuster_kv_requests(cfg, B), gen.adjuster_kv_requests(cfg, B)
+        for f, d in gen.adjuster_plan(cfg, B):
+            assert dl.adjuster_step(f, d, s1) == rl.adjuster_step(f, d, s2)
+            pt = dl.page_table()
+            assert np.array_equal(pt, base.pt) and np.array_equal(rl.page_table(), pt)
+            ptd = torch.from_numpy(pt.copy()).cuda()        # re-issued page table
+            o = run(cfg, x, lgd, base.pool, ptd, bufs)
+            assert torch.equal(o.y, y0)
