@@ -76,7 +76,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--tokens", type=int, default=0, help="override T (decode sweep)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

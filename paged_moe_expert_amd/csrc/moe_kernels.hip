@@ -616,6 +616,7 @@ rimuru_status check_shapes(int64_t T, int E, int k, int H, int I, int dtype) {
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED>
 hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  if (g.N % BN != 0 || g.K % BK != 0) return hipErrorInvalidValue;  // tiles must cover C exactly
   uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
   uint64_t grid = (blocks + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
@@ -624,12 +625,23 @@ hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   return hipGetLastError();
 }
 
+// fp32 tiles take a shorter K step, keeping their LDS footprint near the bf16
+// tiles'. Column tiles are 128 wide when N allows it, else 64 (N is a
+// multiple of 64 by validation).
 template <typename T, bool GATED>
 hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  constexpr bool kF32 = sizeof(T) == 4;
+  constexpr int BK_STREAM = kF32 ? 16 : 64;
+  constexpr int BK_TILE = kF32 ? 16 : 32;
+  const bool wide = g.N % 128 == 0;
   switch (p.id) {
-    case kPlan16: return launch_gemm<T, 16, 64, 64, 1, 4, 1, GATED>(g, tiles_max, st);
-    case kPlan64: return launch_gemm<T, 64, 128, 32, 2, 2, 4, GATED>(g, tiles_max, st);
-    default: return launch_gemm<T, 128, 128, 32, 2, 2, 8, GATED>(g, tiles_max, st);
+    case kPlan16: return launch_gemm<T, 16, 64, BK_STREAM, 1, 4, 1, GATED>(g, tiles_max, st);
+    case kPlan64:
+      return wide ? launch_gemm<T, 64, 128, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st)
+                  : launch_gemm<T, 64, 64, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st);
+    default:
+      return wide ? launch_gemm<T, 128, 128, BK_TILE, 2, 2, 8, GATED>(g, tiles_max, st)
+                  : launch_gemm<T, 128, 64, BK_TILE, 2, 2, 8, GATED>(g, tiles_max, st);
   }
 }
 

@@ -76,6 +76,7 @@ CUSTOM = [
     ("bf16-big-skewed", 16, 4, 256, 128, 1000, "bf16", 8 * KIB, [4, 3, 2.5, 2] + [0] * 10 + [-50, -50]),
     ("f32-mid-tiles", 8, 2, 128, 64, 500, "f32", 4 * KIB, None),
     ("f32-big-tiles", 8, 2, 128, 64, 1500, "f32", 4 * KIB, None),
+    ("bf16-narrow-inter-big-tiles", 8, 2, 128, 64, 1500, "bf16", 4 * KIB, None),
     ("bf16-k1", 4, 1, 128, 64, 33, "bf16", 4 * KIB, None),
     ("bf16-k-equals-E", 8, 8, 128, 192, 19, "bf16", 4 * KIB, None),
     ("bf16-one-expert", 1, 1, 192, 64, 50, "bf16", 4 * KIB, None),
