@@ -187,15 +187,15 @@ typedef struct {
   int32_t P;           /* pages per projection in pt; P*page_bytes >= H*I*es */
   int32_t dtype;       /* RIMURU_BF16 or RIMURU_F32: x, weights and y share it */
   int32_t renormalize; /* must be 1: the kept top-k weights sum to one */
-  const void* x;       /* [T, H] tokens */
+  const void* x;       /* [T, H] tokens, 16-byte aligned */
   const float* logits; /* [T, E] fp32 router logits; finite (precondition) */
   const void* pool_base; /* pool start, 256-byte aligned */
   const int32_t* pt;   /* [E][3][P] page indices in units of page_bytes; every
                           entry an expert with routed tokens uses must lie in
                           the pool (precondition, not checked per call) */
   uint64_t page_bytes; /* expert-view page, a multiple of 128 */
-  void* y;             /* [T, H] output, dtype */
-  int32_t* topk_ids;   /* [T, k] out: expert ids in rank order */
+  void* y;             /* [T, H] output, dtype, 16-byte aligned */
+  int32_t* topk_ids;   /* [T, k] out: expert ids in rank order, 16-byte aligned */
   float* topk_w;       /* [T, k] out: renormalised weights */
   int32_t* sorted_ids; /* [sorted_len] out: routed slots t*k + j grouped by expert
                           (ascending expert, ascending slot), each expert's
@@ -216,12 +216,13 @@ typedef struct {
  * gate/up GEMM with SiLU, down GEMM with routing weight, top-k combine. */
 #define RIMURU_MOE_STAGES 6
 
-/* Buffer sizes for a call with these shapes: sorted_len (entries of
- * sorted_ids), workspace_bytes, and the tile height block_m the segments are
- * padded to. Any output pointer may be NULL. The workspace does not depend
- * on the size of the expert weights: the layer never copies them.
+/* Buffer sizes for a call with these shapes and P pages per projection:
+ * sorted_len (entries of sorted_ids), workspace_bytes, and the tile height
+ * block_m the segments are padded to. Any output pointer may be NULL. The
+ * workspace does not depend on the size of the expert weights: the layer
+ * never copies them.
  * Errors: EINVAL, EDTYPE. */
-rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t P,
                                int32_t dtype, uint64_t* sorted_len,
                                uint64_t* workspace_bytes, int32_t* block_m);
 

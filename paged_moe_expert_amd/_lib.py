@@ -60,7 +60,7 @@ _PROTOS = {
     "rimuru_view_usage": (C.c_int32, [C.c_void_p, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
     "rimuru_pool_stats": (C.c_int32, [C.c_void_p, C.POINTER(PoolStats)]),
     "rimuru_pool_check": (C.c_int32, [C.c_void_p]),
-    "rimuru_moe_sizes": (C.c_int32, [C.c_int32] * 6 + [C.POINTER(C.c_uint64), C.POINTER(C.c_uint64),
+    "rimuru_moe_sizes": (C.c_int32, [C.c_int32] * 7 + [C.POINTER(C.c_uint64), C.POINTER(C.c_uint64),
                                                       C.POINTER(C.c_int32)]),
     "rimuru_fused_moe_paged": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p]),
     "rimuru_pt_check": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_uint64, C.c_uint64]),

@@ -96,6 +96,11 @@ struct Elt<uint16_t> {
   static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) {
     return (s[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
   }
+  // 8 consecutive K values per lane (one 16-byte segment): one MFMA
+  static constexpr int SEG8 = 1;
+  static __device__ __forceinline__ f32x4 mma8(const u32x4* a, const u32x4* b, f32x4 c) {
+    return mma(a[0], b[0], c);
+  }
 };
 
 template <>
@@ -113,6 +118,15 @@ struct Elt<float> {
   static __device__ __forceinline__ uint32_t from_f32(float v) { return __float_as_uint(v); }
   static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
   static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) { return s[c]; }
+  // 8 consecutive K values per lane (two 16-byte segments): eight K=4 MFMAs,
+  // MFMA kk taking K value kk of every lane's group.
+  static constexpr int SEG8 = 2;
+  static __device__ __forceinline__ f32x4 mma8(const u32x4* a, const u32x4* b, f32x4 c) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      c = mma(__uint_as_float(a[kk >> 2][kk & 3]), __uint_as_float(b[kk >> 2][kk & 3]), c);
+    return c;
+  }
 };
 
 // ---------------------------------------------------------------- stage 1: gating
@@ -149,19 +163,26 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// Top-k of one token's logits by one wavefront. Lane r < k ends with the
+// r-th expert (rank order) in *e_out and its logit in *l_out; every lane gets
+// the weight denominator's terms in rank order via the returned softmax value.
 template <int EPL>
-__global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits, int T, int E,
-                                                int k, int32_t* __restrict__ ids,
-                                                float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + static_cast<int64_t>(t) * E;
+__device__ __forceinline__ void load_logits(const float* row, int E, int lane, float (&v)[EPL]) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < E) ? row[e] : 0.0f;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void select_topk_vals(const float (&v)[EPL], int E, int k, int lane,
+                                                 uint32_t* e_out, float* w_out) {
   uint64_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     int e = lane + 64 * i;
-    key[i] = (e < E) ? rank_key(row[e], static_cast<uint32_t>(e)) : 0ull;
+    key[i] = (e < E) ? rank_key(v[i], static_cast<uint32_t>(e)) : 0ull;
   }
   uint32_t my_e = 0;
   float my_l = 0.0f;
@@ -179,23 +200,64 @@ __global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits
       my_l = key_logit(best);
     }
   }
+  // softmax over the kept logits = renormalised full softmax; the sum runs
+  // over the kept experts in rank order
   const float m = __shfl(my_l, 0, 64);
   const float ex = (lane < k) ? expf(my_l - m) : 0.0f;
-  const float s = wave_sum_f32(ex);
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += __shfl(ex, j, 64);
+  *e_out = my_e;
+  *w_out = ex / s;
+}
+
+template <int EPL>
+__device__ __forceinline__ void select_topk(const float* row, int E, int k, int lane,
+                                            uint32_t* e_out, float* w_out) {
+  float v[EPL];
+  load_logits<EPL>(row, E, lane, v);
+  select_topk_vals<EPL>(v, E, k, lane, e_out, w_out);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits, int T, int E,
+                                                int k, int32_t* __restrict__ ids,
+                                                float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  uint32_t e;
+  float wt;
+  select_topk<EPL>(logits + static_cast<int64_t>(t) * E, E, k, lane, &e, &wt);
   if (lane < k) {
-    ids[static_cast<int64_t>(t) * k + lane] = static_cast<int32_t>(my_e);
-    w[static_cast<int64_t>(t) * k + lane] = ex / s;
+    ids[static_cast<int64_t>(t) * k + lane] = static_cast<int32_t>(e);
+    w[static_cast<int64_t>(t) * k + lane] = wt;
   }
 }
 
 // ---------------------------------------------------------------- stage 2: count
 
+// ids is 16-byte aligned (validated); 8 independent 16-byte loads per thread
+// are in flight per round.
 __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int TK,
                                                int32_t* __restrict__ counts) {
   __shared__ int part[4];
   const int e = blockIdx.x;
+  const int n4 = TK >> 2;
+  const u32x4* v = reinterpret_cast<const u32x4*>(ids);
+  const uint32_t ue = static_cast<uint32_t>(e);
   int c = 0;
-  for (int f = threadIdx.x; f < TK; f += 256) c += (ids[f] == e);
+  for (int base = 0; base < n4; base += 256 * 8) {
+    u32x4 r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 256 + threadIdx.x;
+      r[u] = (i < n4) ? v[i] : u32x4{~0u, ~0u, ~0u, ~0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      c += (r[u][0] == ue) + (r[u][1] == ue) + (r[u][2] == ue) + (r[u][3] == ue);
+  }
+  for (int f = n4 * 4 + threadIdx.x; f < TK; f += 256) c += (ids[f] == e);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
@@ -227,7 +289,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   return before + incl - v;
 }
 
-constexpr int kSortChunk = 16;  // consecutive slots per thread per round
+constexpr int kSortChunk = 64;  // consecutive slots per thread per round (16 x 16-byte loads)
 
 __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
                                                     int BM, const int32_t* __restrict__ counts,
@@ -237,6 +299,7 @@ __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ 
   __shared__ int sh[4];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const uint32_t ue = static_cast<uint32_t>(e);
   // start of this expert's padded segment, and the padded total
   int before = 0, total = 0;
   for (int e2 = tid; e2 < E; e2 += 256) {
@@ -253,20 +316,34 @@ __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ 
     expert_off[e] = seg;
     if (e == 0) expert_off[E] = sum_total;
   }
+  const bool vec = (TK & 3) == 0;
   int running = 0;
   for (int base = 0; base < TK; base += 256 * kSortChunk) {
     const int f0 = base + tid * kSortChunk;
-    uint32_t mask = 0;
+    uint64_t mask = 0;
+    if (vec) {
+      u32x4 r[kSortChunk / 4];
 #pragma unroll
-    for (int i = 0; i < kSortChunk; ++i) {
-      int f = f0 + i;
-      if (f < TK && ids[f] == e) mask |= 1u << i;
+      for (int u = 0; u < kSortChunk / 4; ++u)
+        r[u] = (f0 + 4 * u < TK) ? *reinterpret_cast<const u32x4*>(ids + f0 + 4 * u)
+                                 : u32x4{~0u, ~0u, ~0u, ~0u};
+#pragma unroll
+      for (int u = 0; u < kSortChunk / 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mask |= static_cast<uint64_t>(r[u][c] == ue) << (4 * u + c);
+    } else {
+      for (int i = 0; i < kSortChunk; ++i) {
+        const int f = f0 + i;
+        if (f < TK && ids[f] == e) mask |= 1ull << i;
+      }
     }
     int chunk_total;
-    int pos = seg + running + block_excl_scan(__popc(mask), &chunk_total, sh);
-#pragma unroll
-    for (int i = 0; i < kSortChunk; ++i)
-      if (mask & (1u << i)) sorted_ids[pos++] = f0 + i;
+    int pos = seg + running + block_excl_scan(__popcll(mask), &chunk_total, sh);
+    while (mask) {
+      const int i = __ffsll(static_cast<long long>(mask)) - 1;
+      sorted_ids[pos++] = f0 + i;
+      mask &= mask - 1;
+    }
     running += chunk_total;
   }
   const int padded = (cnt + BM - 1) / BM * BM;
@@ -508,6 +585,230 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- stages 4, 5 for few rows: weight streaming
+
+// Few routed rows per expert: the GEMM is a weight stream. A workgroup owns
+// one 16-row tile and BN columns; its ksplit wavefronts each own a
+// contiguous K range and stream their weight rows with DEPTH steps of loads
+// in flight. Each step a wavefront transposes its own 32 x BN weight slice
+// through a private LDS buffer (LDS operations of one wavefront complete in
+// issue order, so no barrier is needed) and runs the MFMAs; the A operand is
+// loaded straight into registers. The ksplit partial sums are added in fixed
+// wavefront order at the end, so results are deterministic.
+constexpr int kStreamMaxWaves = 4;
+constexpr int kStreamK = 32;      // K rows per wavefront step
+constexpr int kStreamPtMax = 4096; // page-table entries a workgroup stages in LDS
+
+// NSTEPS > 0: the wavefront's step count is known at compile time and the K
+// loop unrolls into straight-line code (a loop back-edge makes the compiler
+// wait for every load in flight at the loop head). NSTEPS == 0: runtime loop.
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS>
+__global__ __launch_bounds__(kStreamMaxWaves * 64, 3) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
+  typedef Elt<T> X;
+  constexpr int NB = GATED ? 2 : 1;
+  constexpr int VEC = X::VEC;
+  constexpr int CG = BN / VEC;                 // 16-byte column groups per weight row
+  constexpr int RG = 64 / CG;                  // row groups per wavefront
+  constexpr int RPL = kStreamK / RG;           // consecutive weight rows per lane
+  constexpr int TN = BN / 16;
+  constexpr int KP = kStreamK + 16 / X::ES;    // LDS pitch (elements), 16 bytes of padding
+  constexpr int SEG8 = X::SEG8;
+  constexpr int WORDS = RPL * X::ES / 4;       // packed 32-bit words per column
+  static_assert(CG * RG == 64 && RPL * RG == kStreamK && (WORDS == 1 || WORDS == 2 || WORDS % 4 == 0),
+                "stream tile shape");
+  static_assert(NB * 16 * BN * 4 <= NB * BN * KP * X::ES, "reduction must fit the wave buffer");
+
+  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves][NB * BN * KP];
+  extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
+
+  const int nN = a.N / BN;
+  const int n_tiles = a.expert_off[a.E] / 16;
+  const int L = n_tiles * nN;
+  const int chunk = (L + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  if (idx >= chunk) return;
+  const int logical = xcd * chunk + idx;
+  if (logical >= L) return;
+  const int mt = logical / nN;
+  const int nt = logical - mt * nN;
+  const int e = a.tile_expert[mt];
+  const int r0 = mt * 16;
+  const int n0 = nt * BN;
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int fi = lane & 15, fq = lane >> 4;
+  const int kw = a.K / ksplit;
+  const int nsteps = kw / kStreamK;
+  const int kbase = wv * kw;
+
+  // A operand: row fi of the tile, K values fq*8 .. fq*8+7 of each step.
+  // Padding rows read a valid row and are zeroed by a select, so the main
+  // loop has no branch around a load (a branch there makes the compiler wait
+  // for every load in flight at the join).
+  const T* arow;
+  bool a_ok = true;
+  if (a.kdiv > 0) {
+    const int slot = a.sorted_ids[r0 + fi];
+    a_ok = slot < a.TK;
+    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(a_ok ? slot / a.kdiv : 0) * a.lda;
+  } else {
+    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r0 + fi) * a.lda;
+  }
+  const int cg = lane % CG, rg = lane / CG;
+  // Page lookups read LDS: a global load here would make every weight load
+  // wait for all older ones (vector-memory loads retire in order).
+  for (int i = threadIdx.x; i < NB * a.P; i += blockDim.x) {
+    const int b = i / a.P, q = i - b * a.P;
+    pt_lds[i] = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
+  }
+  __syncthreads();
+  const int32_t* pt_row[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) pt_row[b] = pt_lds + b * a.P;
+  const uint32_t col_bytes = static_cast<uint32_t>(n0 + cg * VEC) * X::ES;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
+
+  u32x4 breg[DEPTH][NB][RPL];
+  u32x4 areg[DEPTH][SEG8];
+  f32x4 acc[NB][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  T* wbuf = lds[wv];
+
+  // Loads of step st (clamped to the last step: the surplus loads at the end
+  // repeat addresses already in cache and their data is never used).
+  auto issue = [&](u32x4 (&br)[NB][RPL], u32x4 (&ar)[SEG8], int st) {
+    st = min(st, nsteps - 1);
+    const int k0 = kbase + st * kStreamK;
+#pragma unroll
+    for (int u = 0; u < SEG8; ++u) ar[u] = *reinterpret_cast<const u32x4*>(arow + k0 + fq * 8 + u * VEC);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) {
+        const uint32_t f = static_cast<uint32_t>(k0 + rg * RPL + j) * row_bytes + col_bytes;
+        const uint32_t q = page_index(f, a.pd);
+        const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+        br[b][j] = *reinterpret_cast<const u32x4*>(p);
+      }
+    }
+  };
+
+  // Multiply step data into the accumulators; live == false (a step past the
+  // end) multiplies by a zero A operand, which adds exact zeros.
+  auto consume = [&](const u32x4 (&br)[NB][RPL], const u32x4 (&ar)[SEG8], bool live) {
+    // transpose: column c of the lane's segments gets RPL consecutive K values
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        uint32_t w[WORDS];
+        if constexpr (X::ES == 2) {
+#pragma unroll
+          for (int i = 0; i < WORDS; ++i)
+            w[i] = X::get(br[b][2 * i], c) | (X::get(br[b][2 * i + 1], c) << 16);
+        } else {
+#pragma unroll
+          for (int i = 0; i < WORDS; ++i) w[i] = X::get(br[b][i], c);
+        }
+        T* dst = wbuf + b * BN * KP + (cg * VEC + c) * KP + rg * RPL;
+        if constexpr (WORDS == 1) {
+          *reinterpret_cast<uint32_t*>(dst) = w[0];
+        } else if constexpr (WORDS == 2) {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < WORDS; i += 4)
+            *reinterpret_cast<u32x4*>(dst + i * 4 / X::ES) = u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]};
+        }
+      }
+    }
+    const bool use = live && a_ok;
+    u32x4 af[SEG8];
+#pragma unroll
+    for (int u = 0; u < SEG8; ++u) af[u] = use ? ar[u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 bf[SEG8];
+        const T* src = wbuf + b * BN * KP + (j * 16 + fi) * KP + fq * 8;
+#pragma unroll
+        for (int u = 0; u < SEG8; ++u) bf[u] = *reinterpret_cast<const u32x4*>(src + u * VEC);
+        acc[b][j] = X::mma8(af, bf, acc[b][j]);
+      }
+    }
+  };
+
+  if constexpr (NSTEPS > 0) {
+    // Straight-line pipeline: DEPTH - 1 steps in flight ahead of the one consumed.
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (d < NSTEPS) issue(breg[d], areg[d], d);
+#pragma unroll
+    for (int st = 0; st < NSTEPS; ++st) {
+      if (st + DEPTH - 1 < NSTEPS)
+        issue(breg[(st + DEPTH - 1) % DEPTH], areg[(st + DEPTH - 1) % DEPTH], st + DEPTH - 1);
+      consume(breg[st % DEPTH], areg[st % DEPTH], true);
+    }
+  } else {
+    // Branch-free loop: DEPTH - 1 steps in flight ahead of the one consumed.
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) issue(breg[d], areg[d], d);
+    for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        issue(breg[(d + DEPTH - 1) % DEPTH], areg[(d + DEPTH - 1) % DEPTH], s0 + d + DEPTH - 1);
+        consume(breg[d], areg[d], s0 + d < nsteps);
+      }
+    }
+  }
+
+  // ---- reduce the ksplit partial sums in wavefront order, then the epilogue
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(wbuf);           // [NB][16][BN] of this wavefront
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(b * 16 + 4 * fq + r) * BN + j * 16 + fi] = acc[b][j][r];
+  __syncthreads();
+  constexpr int PER = 4;                                  // outputs per thread per pass
+  T* C = reinterpret_cast<T*>(a.C);
+  for (int o = threadIdx.x * PER; o < 16 * BN; o += blockDim.x * PER) {
+    const int row = o / BN, col = o % BN;
+    float v[NB][PER];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < PER; ++c) v[b][c] = 0.0f;
+    for (int w = 0; w < ksplit; ++w) {
+      const float* rw = reinterpret_cast<const float*>(lds[w]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < PER; ++c) v[b][c] += rw[(b * 16 + row) * BN + col + c];
+    }
+    if constexpr (GATED) {
+      T* dst = C + static_cast<int64_t>(r0 + row) * a.ldc + n0 + col;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) X::put(dst + c, silu(v[0][c]) * v[1][c]);
+    } else {
+      const int slot = a.sorted_ids[r0 + row];
+      if (slot < a.TK) {
+        const float wt = a.topk_w[slot];
+        T* dst = C + static_cast<int64_t>(slot) * a.ldc + n0 + col;
+#pragma unroll
+        for (int c = 0; c < PER; ++c) X::put(dst + c, wt * v[0][c]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- stage 6: combine
 
 template <typename T>
@@ -576,9 +877,9 @@ struct Plan {
   int bm;
 };
 
-Plan choose_plan(int64_t T, int E, int k) {
+Plan choose_plan(int64_t T, int E, int k, int64_t P) {
   int64_t tk = T * k;
-  if (tk <= 24ll * E) return {kPlan16, 16};
+  if (tk <= 24ll * E && 2 * P <= kStreamPtMax) return {kPlan16, 16};
   if (tk <= 160ll * E) return {kPlan64, 64};
   return {kPlan128, 128};
 }
@@ -625,17 +926,48 @@ hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   return hipGetLastError();
 }
 
-// fp32 tiles take a shorter K step, keeping their LDS footprint near the bf16
-// tiles'. Column tiles are 128 wide when N allows it, else 64 (N is a
+template <typename T, int BN, int DEPTH, bool GATED>
+hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  const int ksteps = g.K / kStreamK;
+  const int ksplit = (ksteps % 4 == 0) ? 4 : (ksteps % 2 == 0) ? 2 : 1;
+  if (g.N % BN != 0 || g.K % kStreamK != 0) return hipErrorInvalidValue;
+  uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
+  uint64_t grid = (blocks + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  const dim3 gd(static_cast<uint32_t>(grid)), bd(ksplit * 64);
+  const size_t pt_bytes = static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
+  switch (ksteps / ksplit) {
+#define RIMURU_STREAM_CASE(n) \
+    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n>), gd, bd, pt_bytes, st, g, ksplit); break;
+    RIMURU_STREAM_CASE(2)
+    RIMURU_STREAM_CASE(3)
+    RIMURU_STREAM_CASE(4)
+    RIMURU_STREAM_CASE(6)
+    RIMURU_STREAM_CASE(8)
+    RIMURU_STREAM_CASE(12)
+    RIMURU_STREAM_CASE(16)
+#undef RIMURU_STREAM_CASE
+    // other step counts: runtime loop, one step less in flight (register budget)
+    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0>), gd, bd, pt_bytes, st, g, ksplit);
+  }
+  return hipGetLastError();
+}
+
+// Few rows per expert: the streaming kernel (16-row tiles). Otherwise tiled
+// GEMMs; fp32 tiles take a shorter K step, keeping their LDS footprint near the
+// bf16 tiles'. Column tiles are 128 wide when N allows it, else 64 (N is a
 // multiple of 64 by validation).
 template <typename T, bool GATED>
 hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   constexpr bool kF32 = sizeof(T) == 4;
-  constexpr int BK_STREAM = kF32 ? 16 : 64;
   constexpr int BK_TILE = kF32 ? 16 : 32;
   const bool wide = g.N % 128 == 0;
   switch (p.id) {
-    case kPlan16: return launch_gemm<T, 16, 64, BK_STREAM, 1, 4, 1, GATED>(g, tiles_max, st);
+    case kPlan16:
+      if constexpr (GATED) return launch_stream<T, 64, 3, true>(g, tiles_max, st);
+      else
+        return wide ? launch_stream<T, 128, 3, false>(g, tiles_max, st)
+                    : launch_stream<T, 64, 3, false>(g, tiles_max, st);
     case kPlan64:
       return wide ? launch_gemm<T, 64, 128, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st)
                   : launch_gemm<T, 64, 64, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st);
@@ -658,10 +990,10 @@ hipError_t launch_layer(const rimuru_moe_args* a, Plan p, const Layout& lay, hip
   hipError_t err;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
 
+  const int epl = (E + 63) / 64;
   if ((err = mark(0)) != hipSuccess) return err;
   {
     dim3 grid((T_ + 3) / 4);
-    int epl = (E + 63) / 64;
     if (epl <= 1) hipLaunchKernelGGL(k_gating<1>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
     else if (epl <= 2) hipLaunchKernelGGL(k_gating<2>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
     else if (epl <= 4) hipLaunchKernelGGL(k_gating<4>, grid, dim3(256), 0, st, a->logits, T_, E, k, a->topk_ids, a->topk_w);
@@ -727,11 +1059,12 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 using namespace rimuru;
 
 extern "C" rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
-                                          int32_t dtype, uint64_t* sorted_len,
+                                          int32_t P, int32_t dtype, uint64_t* sorted_len,
                                           uint64_t* workspace_bytes, int32_t* block_m) {
   rimuru_status s = check_shapes(T, E, k, H, I, dtype);
   if (s != RIMURU_OK) return s;
-  Plan p = choose_plan(T, E, k);
+  if (P < 1) return rimuru_fail(RIMURU_EINVAL, "P = %d must be at least 1", P);
+  Plan p = choose_plan(T, E, k, P);
   Layout l = layout_for(T, E, k, H, I, dtype == RIMURU_BF16 ? 2 : 4, p.bm);
   if (sorted_len) *sorted_len = l.sorted_len;
   if (workspace_bytes) *workspace_bytes = l.total;
@@ -759,9 +1092,10 @@ extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* 
   if (!a->x || !a->logits || !a->pool_base || !a->pt || !a->y || !a->topk_ids || !a->topk_w ||
       !a->sorted_ids || !a->expert_off || !a->workspace)
     return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged: a required pointer is NULL");
-  if (!aligned(a->pool_base, 256) || !aligned(a->workspace, 256) || !aligned(a->x, 16) || !aligned(a->y, 16))
-    return rimuru_fail(RIMURU_EINVAL, "pool_base/workspace need 256-byte and x/y 16-byte alignment");
-  Plan p = choose_plan(a->T, a->E, a->k);
+  if (!aligned(a->pool_base, 256) || !aligned(a->workspace, 256) || !aligned(a->x, 16) ||
+      !aligned(a->y, 16) || !aligned(a->topk_ids, 16))
+    return rimuru_fail(RIMURU_EINVAL, "pool_base/workspace need 256-byte and x/y/topk_ids 16-byte alignment");
+  Plan p = choose_plan(a->T, a->E, a->k, a->P);
   Layout lay = layout_for(a->T, a->E, a->k, a->H, a->I, es, p.bm);
   if (a->workspace_bytes < lay.total)
     return rimuru_fail(RIMURU_EINVAL, "workspace of %llu bytes is below the %llu needed",

@@ -126,10 +126,10 @@ def _dtype_code(t) -> int:
     raise RimuruError(-4, "fused_moe_paged", f"unsupported dtype {t.dtype}")
 
 
-def moe_sizes(T: int, E: int, k: int, H: int, I: int, dtype: int):
+def moe_sizes(T: int, E: int, k: int, H: int, I: int, P: int, dtype: int):
     """(sorted_len, workspace_bytes, block_m)."""
     sl, ws, bm = C.c_uint64(), C.c_uint64(), C.c_int32()
-    check(lib().rimuru_moe_sizes(T, E, k, H, I, dtype, C.byref(sl), C.byref(ws), C.byref(bm)),
+    check(lib().rimuru_moe_sizes(T, E, k, H, I, P, dtype, C.byref(sl), C.byref(ws), C.byref(bm)),
           "moe_sizes")
     return sl.value, ws.value, bm.value
 
@@ -137,11 +137,11 @@ def moe_sizes(T: int, E: int, k: int, H: int, I: int, dtype: int):
 class MoeBuffers:
     """Outputs and workspace for one shape; reuse them across calls."""
 
-    def __init__(self, T, E, k, H, I, dtype, device="cuda"):
+    def __init__(self, T, E, k, H, I, P, dtype, device="cuda"):
         import torch
         tdt = torch.bfloat16 if dtype == BF16 else torch.float32
-        sl, ws, bm = moe_sizes(T, E, k, H, I, dtype)
-        self.shape = (T, E, k, H, I, dtype)
+        sl, ws, bm = moe_sizes(T, E, k, H, I, P, dtype)
+        self.shape = (T, E, k, H, I, P, dtype)
         self.block_m = bm
         self.y = torch.empty((T, H), dtype=tdt, device=device)
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
@@ -166,7 +166,7 @@ def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
     P = pt.shape[2]
     dt = _dtype_code(x)
     if bufs is None:
-        bufs = MoeBuffers(T, E, k, H, I, dt, device=x.device)
+        bufs = MoeBuffers(T, E, k, H, I, P, dt, device=x.device)
     a = MoeArgs()
     a.T, a.E, a.k, a.H, a.I, a.P, a.dtype, a.renormalize = T, E, k, H, I, P, dt, 1
     a.x, a.logits, a.pool_base, a.pt = x.data_ptr(), logits.data_ptr(), pool.data_ptr(), pt.data_ptr()

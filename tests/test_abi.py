@@ -38,28 +38,31 @@ def test_abi_version_and_error_text():
 
 
 def test_moe_sizes_and_plans():
-    sl, ws, bm = R.moe_sizes(64, 128, 8, 2048, 768, R.BF16)
+    sl, ws, bm = R.moe_sizes(64, 128, 8, 2048, 768, 1, R.BF16)
     assert bm == 16 and sl % bm == 0 and sl >= 64 * 8
     # tiles bound: floor(T*k/bm) + min(E, T*k)
     assert sl == (512 // 16 + 128) * 16
     # the workspace never scales with expert weight bytes: only with tokens
     assert ws < 16 * 2 ** 20
-    sl4, ws4, bm4 = R.moe_sizes(8192, 128, 8, 2048, 768, R.BF16)
+    sl4, ws4, bm4 = R.moe_sizes(8192, 128, 8, 2048, 768, 48, R.BF16)
     assert bm4 == 128
-    _, _, bm3 = R.moe_sizes(2048, 256, 8, 2048, 512, R.BF16)
+    _, _, bm3 = R.moe_sizes(2048, 256, 8, 2048, 512, 1, R.BF16)
     assert bm3 == 64
-    sl1, _, bm1 = R.moe_sizes(1, 128, 8, 2048, 768, R.BF16)
+    sl1, _, bm1 = R.moe_sizes(1, 128, 8, 2048, 768, 1, R.BF16)
     assert bm1 == 16 and sl1 == 8 * 16
+    # too many pages per projection for the streaming plan: the tiled plan takes it
+    _, _, bmp = R.moe_sizes(64, 128, 8, 2048, 768, 3000, R.BF16)
+    assert bmp == 64
     with pytest.raises(_lib.RimuruError) as e:
-        R.moe_sizes(4, 8, 9, 128, 64, R.F32)
+        R.moe_sizes(4, 8, 9, 128, 64, 8, R.F32)
     assert e.value.status == _lib.EINVAL
     with pytest.raises(_lib.RimuruError) as e:
-        R.moe_sizes(4, 8, 2, 128, 64, 7)
+        R.moe_sizes(4, 8, 2, 128, 64, 8, 7)
     assert e.value.status == _lib.EDTYPE
     with pytest.raises(_lib.RimuruError):
-        R.moe_sizes(4, 8, 2, 100, 64, R.F32)          # H not a multiple of 64
+        R.moe_sizes(4, 8, 2, 100, 64, 8, R.F32)          # H not a multiple of 64
     with pytest.raises(_lib.RimuruError):
-        R.moe_sizes(4, 600, 2, 128, 64, R.F32)        # E above 512
+        R.moe_sizes(4, 600, 2, 128, 64, 8, R.F32)        # E above 512
 
 
 def _args(**over):

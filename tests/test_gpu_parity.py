@@ -215,7 +215,7 @@ def test_decode_sweep_under_adjuster_steps():
         say(f"[cfg5] batch {B}")
         xb, lg = gen.x_bits(cfg, B), gen.logits(cfg, B)
         x, lgd = to_dev_bits(xb, cfg.dtype), torch.from_numpy(lg).cuda()
-        bufs = R.MoeBuffers(B, cfg.E, cfg.k, cfg.H, cfg.I, R.BF16)
+        bufs = R.MoeBuffers(B, cfg.E, cfg.k, cfg.H, cfg.I, cfg.P, R.BF16)
         out = run(cfg, x, lgd, base.pool, base.ptd, bufs)
         y0 = out.y.clone()
         toks = _sample(B, 16, B)
