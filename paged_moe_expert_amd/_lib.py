@@ -9,7 +9,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librimuru.so")
+# RIMURU_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("RIMURU_LIB") or os.path.join(HERE, "librimuru.so")
 
 OK, EINVAL, ENOMEM, ERANGE, EDTYPE, EHIP, EBUSY = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1

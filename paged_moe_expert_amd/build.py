@@ -35,9 +35,10 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + SOURCES + ["-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out`; defines are extra -D macros (tile tuning)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + flags() + [f"-D{d}" for d in defines] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,8 +48,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -35,8 +35,10 @@ namespace rimuru {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxK = 32;
 constexpr int kMaxE = 512;
@@ -96,6 +98,32 @@ struct Elt<uint16_t> {
   static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) {
     return (s[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
   }
+  // B operand of a 32x32x16 MFMA from a row-major [K][N] LDS tile (pitch in
+  // elements): lane l needs B[k0 + 8*(l/32) .. +7][n0 + l%32]. Two transposed
+  // LDS reads (ds_read_b64_tr_b16) deliver it: in each 16-lane group, source
+  // lane s points at B[k0 + s/4][n0 + 4*(s%4)] and output lane i receives
+  // B[k0 .. k0+3][n0 + i].
+  static constexpr int B_PAD = 32;   // row padding (elements): 64 bytes
+  static __device__ __forceinline__ Frag bfrag32(const uint16_t* tile, int pitch, int k0, int n0,
+                                                 int lane) {
+    const int grp = lane >> 4, s = lane & 15;
+    const int row = k0 + 8 * (grp >> 1) + (s >> 2);
+    const int col = n0 + 16 * (grp & 1) + 4 * (s & 3);
+    // tile points into LDS: the generic -> local address-space cast is exact
+    typedef __attribute__((address_space(3))) v4i16 lds_v4;
+    lds_v4* p0 = (lds_v4*)(tile + row * pitch + col);
+    lds_v4* p1 = (lds_v4*)(tile + (row + 4) * pitch + col);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+  // 32x32 output tile, K = 16 per MFMA, 8 values of each operand per lane
+  static constexpr int KI32 = 16;
+  static __device__ __forceinline__ f32x16 mma32(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
   // 8 consecutive K values per lane (one 16-byte segment): one MFMA
   static constexpr int SEG8 = 1;
   static __device__ __forceinline__ f32x4 mma8(const u32x4* a, const u32x4* b, f32x4 c) {
@@ -118,6 +146,17 @@ struct Elt<float> {
   static __device__ __forceinline__ uint32_t from_f32(float v) { return __float_as_uint(v); }
   static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
   static __device__ __forceinline__ uint32_t get(const u32x4& s, int c) { return s[c]; }
+  // B operand of a 32x32x2 MFMA from a row-major [K][N] LDS tile: lane l
+  // needs B[k0 + l/32][n0 + l%32], one plain read.
+  static constexpr int B_PAD = 4;    // row padding (elements): 16 bytes
+  static __device__ __forceinline__ Frag bfrag32(const float* tile, int pitch, int k0, int n0, int lane) {
+    return tile[(k0 + (lane >> 5)) * pitch + n0 + (lane & 31)];
+  }
+  // 32x32 output tile, K = 2 per MFMA, one value of each operand per lane
+  static constexpr int KI32 = 2;
+  static __device__ __forceinline__ f32x16 mma32(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
   // 8 consecutive K values per lane (two 16-byte segments): eight K=4 MFMAs,
   // MFMA kk taking K value kk of every lane's group.
   static constexpr int SEG8 = 2;
@@ -373,29 +412,39 @@ struct GemmArgs {
 };
 
 // One workgroup computes a BM x BN tile of C (two tiles, w1 and w3, when
-// GATED). WM x WN wavefronts each own a (BM/WM) x (BN/WN) block of 16x16
+// GATED). WM x WN wavefronts each own a (BM/WM) x (BN/WN) block of 32x32
 // MFMA tiles. K advances BK at a time through a double-buffered LDS stage:
-// A rows stored K-contiguous; weight tiles, which are N-contiguous in the
-// pool, are transposed in registers on their way into LDS so every MFMA
-// operand is one 16-byte LDS read per lane.
-template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED>
+// A rows are stored K-contiguous; weight rows are stored as they sit in the
+// pool (N-contiguous, row pitch padded against bank conflicts) and the MFMA
+// B operand is gathered by LDS transpose reads. PT_LDS stages the expert's
+// page-table rows in LDS (dynamic shared memory) so a page lookup never waits
+// on a global load.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED, bool PT_LDS, int NBUF>
 __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
   typedef Elt<T> X;
   constexpr int NT = WM * WN * 64;
   constexpr int VEC = X::VEC;
   constexpr int NB = GATED ? 2 : 1;
-  constexpr int BKP = BK + VEC;                  // 16 bytes of row padding
+  constexpr int BKP = BK + VEC;                  // A row pitch: 16 bytes of padding
+  constexpr int BNP = BN + X::B_PAD;             // B row pitch
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int KI = X::KI32;
+  constexpr int FE = KI / 2;                     // operand values per lane per MFMA
   constexpr int A_SEGS = BM * BK / VEC;
   constexpr int A_LOADS = (A_SEGS + NT - 1) / NT;
   constexpr int RK = BK * BN / (VEC * NT);       // weight rows per thread per matrix
   constexpr int CG = BN / VEC;                   // 16-byte column groups per weight row
   static_assert(RK >= 1 && RK * VEC * NT == BK * BN, "weight tile must split evenly");
-  static_assert(BK % RK == 0 && WTM % 16 == 0 && WTN % 16 == 0 && BK % X::KI == 0, "tile shape");
+  static_assert(BK % RK == 0 && WTM % 32 == 0 && WTN % 32 == 0 && BK % KI == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM * BKP];
-  __shared__ __attribute__((aligned(16))) T Bs[2][NB][BN * BKP];
+  // NBUF == 2: double-buffered stages, one barrier per step. NBUF == 1: one
+  // buffer (half the LDS, so larger stages fit); the next stage waits in
+  // registers during the MFMAs and is written between two barriers.
+  static_assert(NBUF == 1 || NBUF == 2, "one or two LDS stages");
+  __shared__ __attribute__((aligned(16))) T As[NBUF][BM * BKP];
+  __shared__ __attribute__((aligned(16))) T Bs[NBUF][NB][BK * BNP];
+  extern __shared__ int32_t pt_lds[];
 
   // ---- tile assignment: each XCD (dispatch round-robins over 8) takes one
   // contiguous chunk of the live tiles, walked GM row-tiles at a time.
@@ -422,50 +471,59 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
   const int lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WN, wn = wv % WN;
 
-  // ---- A row sources for this tile
+  // ---- page-table rows of this expert
+  const int32_t* pt_row[NB];
+  if constexpr (PT_LDS) {
+    for (int i = tid; i < NB * a.P; i += NT) {
+      const int b = i / a.P, q = i - b * a.P;
+      pt_lds[i] = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) pt_row[b] = pt_lds + b * a.P;
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) pt_row[b] = a.pt + static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P;
+  }
+
+  // ---- A row sources for this tile (padding rows read row 0 and are zeroed)
   const T* a_src[A_LOADS];
+  bool a_ok[A_LOADS];
   int a_row[A_LOADS], a_kv[A_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
-    int s = tid + i * NT;
-    a_row[i] = s / (BK / VEC);
-    a_kv[i] = s % (BK / VEC);
-    a_src[i] = nullptr;
-    if (s < A_SEGS) {
-      int r = r0 + a_row[i];
+    const int sidx = tid + i * NT;
+    a_row[i] = sidx / (BK / VEC);
+    a_kv[i] = sidx % (BK / VEC);
+    a_ok[i] = sidx < A_SEGS;
+    int64_t src_row = 0;
+    if (a_ok[i]) {
+      const int r = r0 + a_row[i];
       if (a.kdiv > 0) {
-        int slot = a.sorted_ids[r];
-        if (slot < a.TK)
-          a_src[i] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(slot / a.kdiv) * a.lda;
+        const int slot = a.sorted_ids[r];
+        a_ok[i] = slot < a.TK;
+        src_row = a_ok[i] ? slot / a.kdiv : 0;
       } else {
-        a_src[i] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r) * a.lda;
+        src_row = r;
       }
     }
+    a_src[i] = reinterpret_cast<const T*>(a.A) + src_row * a.lda + a_kv[i] * VEC;
   }
-  // ---- weight segment of this thread: rows rb*RK .. +RK-1, columns cb*VEC .. +VEC-1
   const int cb = tid % CG, rb = tid / CG;
-  const int32_t* pt_row[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) pt_row[b] = a.pt + static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P;
+  const uint32_t col_bytes = static_cast<uint32_t>(n0 + cb * VEC) * X::ES;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
 
   u32x4 a_reg[A_LOADS];
   u32x4 b_reg[NB][RK];
 
   auto load_stage = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      if (a_src[i] != nullptr)
-        a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK + a_kv[i] * VEC);
-      else
-        a_reg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < A_LOADS; ++i) a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int j = 0; j < RK; ++j) {
-        uint32_t row = static_cast<uint32_t>(kt * BK + rb * RK + j);
-        uint32_t f = (row * static_cast<uint32_t>(a.N) + static_cast<uint32_t>(n0 + cb * VEC)) * X::ES;
-        uint32_t q = page_index(f, a.pd);
+        const uint32_t f = static_cast<uint32_t>(kt * BK + rb * RK + j) * row_bytes + col_bytes;
+        const uint32_t q = page_index(f, a.pd);
         const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
         b_reg[b][j] = *reinterpret_cast<const u32x4*>(p);
       }
@@ -475,100 +533,79 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
-      if (tid + i * NT < A_SEGS)
-        *reinterpret_cast<u32x4*>(&As[buf][a_row[i] * BKP + a_kv[i] * VEC]) = a_reg[i];
-    }
-    // transpose: column c of the segment gets RK consecutive K values
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        T* dst = &Bs[buf][b][(cb * VEC + c) * BKP + rb * RK];
-        if constexpr (X::ES * RK == 2) {
-          *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(X::get(b_reg[b][0], c));
-        } else if constexpr (X::ES * RK == 4) {
-          uint32_t v = (X::ES == 2) ? (X::get(b_reg[b][0], c) | (X::get(b_reg[b][1], c) << 16))
-                                    : X::get(b_reg[b][0], c);
-          *reinterpret_cast<uint32_t*>(dst) = v;
-        } else if constexpr (X::ES * RK == 8) {
-          u32x2 v;
-          if constexpr (X::ES == 2) {
-            v[0] = X::get(b_reg[b][0], c) | (X::get(b_reg[b][1], c) << 16);
-            v[1] = X::get(b_reg[b][2], c) | (X::get(b_reg[b][3], c) << 16);
-          } else {
-            v[0] = X::get(b_reg[b][0], c);
-            v[1] = X::get(b_reg[b][1], c);
-          }
-          *reinterpret_cast<u32x2*>(dst) = v;
-        } else {
-          static_assert(X::ES * RK == 16, "unsupported weight rows per thread");
-          u32x4 v;
-          if constexpr (X::ES == 2) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              v[j] = X::get(b_reg[b][2 * j], c) | (X::get(b_reg[b][2 * j + 1], c) << 16);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = X::get(b_reg[b][j], c);
-          }
-          *reinterpret_cast<u32x4*>(dst) = v;
-        }
+      if (tid + i * NT < A_SEGS) {
+        const u32x4 v = a_ok[i] ? a_reg[i] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&As[buf][a_row[i] * BKP + a_kv[i] * VEC]) = v;
       }
     }
+    // weight rows as they are: 16-byte segments, row pitch BNP
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < RK; ++j)
+        *reinterpret_cast<u32x4*>(&Bs[buf][b][(rb * RK + j) * BNP + cb * VEC]) = b_reg[b][j];
   };
 
-  f32x4 acc[NB][TM][TN];
+  f32x16 acc[NB][TM][TN];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
 
   const int nk = a.K / BK;
-  const int fi = lane & 15, fq = lane >> 4;  // operand row/column and K group of this lane
+  const int fi = lane & 31, fq = lane >> 5;  // operand row/column and K half of this lane
 
+  if constexpr (PT_LDS) __syncthreads();
   load_stage(0);
   store_stage(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
+    const int buf = (NBUF == 2) ? (kt & 1) : 0;
     if (kt + 1 < nk) load_stage(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / X::KI; ++kk) {
+    for (int kk = 0; kk < BK / KI; ++kk) {
       typename X::Frag af[TM], bfr[NB][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = X::frag(&As[buf][(wm * WTM + i * 16 + fi) * BKP + kk * X::KI + fq * X::FE]);
+        af[i] = X::frag(&As[buf][(wm * WTM + i * 32 + fi) * BKP + kk * KI + fq * FE]);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[b][j] = X::frag(&Bs[buf][b][(wn * WTN + j * 16 + fi) * BKP + kk * X::KI + fq * X::FE]);
+          bfr[b][j] = X::bfrag32(Bs[buf][b], BNP, kk * KI, wn * WTN + j * 32, lane);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[b][i][j] = X::mma(af[i], bfr[b][j], acc[b][i][j]);
+          for (int j = 0; j < TN; ++j) acc[b][i][j] = X::mma32(af[i], bfr[b][j], acc[b][i][j]);
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
+    if constexpr (NBUF == 2) {
+      if (kt + 1 < nk) store_stage(buf ^ 1);
+      __syncthreads();
+    } else if (kt + 1 < nk) {
+      __syncthreads();
+      store_stage(0);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
+  // ---- epilogue: acc[r] of a 32x32 tile is row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
   T* C = reinterpret_cast<T*>(a.C);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r0 + wm * WTM + i * 16 + 4 * fq + r;
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
       if constexpr (GATED) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WTN + j * 16 + fi;
-          float v = silu(acc[0][i][j][r]) * acc[1][i][j][r];
-          X::put(&C[static_cast<int64_t>(row) * a.ldc + col], v);
+          const int col = n0 + wn * WTN + j * 32 + fi;
+          X::put(&C[static_cast<int64_t>(row) * a.ldc + col], silu(acc[0][i][j][r]) * acc[1][i][j][r]);
         }
       } else {
         const int slot = a.sorted_ids[row];
@@ -576,7 +613,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
           const float wt = a.topk_w[slot];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + fi;
+            const int col = n0 + wn * WTN + j * 32 + fi;
             X::put(&C[static_cast<int64_t>(slot) * a.ldc + col], wt * acc[0][i][j][r]);
           }
         }
@@ -915,14 +952,41 @@ rimuru_status check_shapes(int64_t T, int E, int k, int H, int I, int dtype) {
   return RIMURU_OK;
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED>
+constexpr int kTilePtMax = 4096;  // page-table entries a tiled workgroup stages in LDS
+
+// bf16 tile shapes of the tiled plans (compile-time overridable for tuning
+// sweeps): column tile, K step, wavefront grid, LDS stages. UP is the gated
+// gate/up GEMM, DN the down GEMM; T128 the 128-row plan, T64 the 64-row one.
+#ifndef RIMURU_T128_UP
+#define RIMURU_T128_UP 128, 64, 2, 4, 1
+#endif
+#ifndef RIMURU_T128_DN
+#define RIMURU_T128_DN 256, 64, 2, 4, 1
+#endif
+#ifndef RIMURU_T64_UP
+#define RIMURU_T64_UP 128, 64, 2, 4, 1
+#endif
+#ifndef RIMURU_T64_DN
+#define RIMURU_T64_DN 256, 64, 2, 2, 1
+#endif
+struct TileShape { int bn, bk, wm, wn, nbuf; };
+constexpr TileShape kT128Up{RIMURU_T128_UP}, kT128Dn{RIMURU_T128_DN};
+constexpr TileShape kT64Up{RIMURU_T64_UP}, kT64Dn{RIMURU_T64_DN};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int GM, bool GATED, int NBUF = 2>
 hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   if (g.N % BN != 0 || g.K % BK != 0) return hipErrorInvalidValue;  // tiles must cover C exactly
   uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
   uint64_t grid = (blocks + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_paged_gemm<T, BM, BN, BK, WM, WN, GM, GATED>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(WM * WN * 64), 0, st, g);
+  const int nb = GATED ? 2 : 1;
+  if (nb * g.P <= kTilePtMax) {
+    hipLaunchKernelGGL((k_paged_gemm<T, BM, BN, BK, WM, WN, GM, GATED, true, NBUF>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(WM * WN * 64), static_cast<size_t>(nb) * g.P * sizeof(int32_t), st, g);
+  } else {
+    hipLaunchKernelGGL((k_paged_gemm<T, BM, BN, BK, WM, WN, GM, GATED, false, NBUF>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(WM * WN * 64), 0, st, g);
+  }
   return hipGetLastError();
 }
 
@@ -960,7 +1024,7 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
 template <typename T, bool GATED>
 hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   constexpr bool kF32 = sizeof(T) == 4;
-  constexpr int BK_TILE = kF32 ? 16 : 32;
+  constexpr int BK_TILE = kF32 ? 16 : 64;
   const bool wide = g.N % 128 == 0;
   switch (p.id) {
     case kPlan16:
@@ -969,9 +1033,17 @@ hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_
         return wide ? launch_stream<T, 128, 3, false>(g, tiles_max, st)
                     : launch_stream<T, 64, 3, false>(g, tiles_max, st);
     case kPlan64:
+      if constexpr (!kF32) {
+        constexpr TileShape t = GATED ? kT64Up : kT64Dn;
+        if (g.N % t.bn == 0) return launch_gemm<T, 64, t.bn, t.bk, t.wm, t.wn, 4, GATED, t.nbuf>(g, tiles_max, st);
+      }
       return wide ? launch_gemm<T, 64, 128, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st)
                   : launch_gemm<T, 64, 64, BK_TILE, 2, 2, 4, GATED>(g, tiles_max, st);
     default:
+      if constexpr (!kF32) {
+        constexpr TileShape t = GATED ? kT128Up : kT128Dn;
+        if (g.N % t.bn == 0) return launch_gemm<T, 128, t.bn, t.bk, t.wm, t.wn, 8, GATED, t.nbuf>(g, tiles_max, st);
+      }
       return wide ? launch_gemm<T, 128, 128, BK_TILE, 2, 2, 8, GATED>(g, tiles_max, st)
                   : launch_gemm<T, 128, 64, BK_TILE, 2, 2, 8, GATED>(g, tiles_max, st);
   }

@@ -82,6 +82,9 @@ CUSTOM = [
     ("bf16-one-expert", 1, 1, 192, 64, 50, "bf16", 4 * KIB, None),
     ("bf16-128B-pages", 4, 2, 64, 64, 21, "bf16", 128, None),
     ("bf16-one-token", 16, 4, 256, 128, 1, "bf16", 4 * KIB, None),
+    # 24576 pages per projection: too many to stage in LDS, read from global
+    ("bf16-huge-page-table", 2, 1, 2048, 768, 300, "bf16", 128, None),
+    ("bf16-huge-page-table-decode", 2, 1, 2048, 768, 8, "bf16", 128, None),
 ]
 
 
