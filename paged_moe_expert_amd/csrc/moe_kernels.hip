@@ -124,6 +124,21 @@ struct Elt<uint16_t> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  // B operand of a 16x16x32 MFMA from a row-major [K][N] LDS tile: lane l
+  // needs B[k0 + 8*(l/16) .. +7][n0 + l%16]; two transposed LDS reads (see
+  // bfrag32: here each 16-lane group covers one K octet).
+  static __device__ __forceinline__ void bfrag16(const uint16_t* tile, int pitch, int k0, int n0,
+                                                 int lane, u32x4 (&out)[1]) {
+    const int grp = lane >> 4, s = lane & 15;
+    const int row = k0 + 8 * grp + (s >> 2);
+    const int col = n0 + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) v4i16 lds_v4;
+    lds_v4* p0 = (lds_v4*)(tile + row * pitch + col);
+    lds_v4* p1 = (lds_v4*)(tile + (row + 4) * pitch + col);
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1));
+    out[0] = u32x4{a[0], a[1], b[0], b[1]};
+  }
   // 8 consecutive K values per lane (one 16-byte segment): one MFMA
   static constexpr int SEG8 = 1;
   static __device__ __forceinline__ f32x4 mma8(const u32x4* a, const u32x4* b, f32x4 c) {
@@ -156,6 +171,13 @@ struct Elt<float> {
   static constexpr int KI32 = 2;
   static __device__ __forceinline__ f32x16 mma32(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  // 8 consecutive K values B[k0 + 8*(l/16) + kk][n0 + l%16] per lane, plain reads
+  static __device__ __forceinline__ void bfrag16(const float* tile, int pitch, int k0, int n0, int lane,
+                                                 u32x4 (&out)[2]) {
+    const float* src = tile + (k0 + 8 * (lane >> 4)) * pitch + n0 + (lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) out[kk >> 2][kk & 3] = __float_as_uint(src[kk * pitch]);
   }
   // 8 consecutive K values per lane (two 16-byte segments): eight K=4 MFMAs,
   // MFMA kk taking K value kk of every lane's group.
@@ -634,13 +656,28 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
 // wavefront order at the end, so results are deterministic.
 constexpr int kStreamMaxWaves = 4;
 constexpr int kStreamK = 32;      // K rows per wavefront step
+// column-tile width and steps in flight of the gate/up and down streams
+// (compile-time overridable for tuning sweeps), and workgroups per CU
+#ifndef RIMURU_STREAM_UP
+#define RIMURU_STREAM_UP 128, 2
+#endif
+#ifndef RIMURU_STREAM_DN
+#define RIMURU_STREAM_DN 256, 2
+#endif
+#ifndef RIMURU_STREAM_WG_PER_CU
+#define RIMURU_STREAM_WG_PER_CU 2
+#endif
+struct StreamShape { int bn, depth; };
+constexpr StreamShape kStreamUp{RIMURU_STREAM_UP}, kStreamDn{RIMURU_STREAM_DN};
+constexpr int kStreamUpBN = kStreamUp.bn, kStreamUpDepth = kStreamUp.depth;
+constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
 constexpr int kStreamPtMax = 4096; // page-table entries a workgroup stages in LDS
 
 // NSTEPS > 0: the wavefront's step count is known at compile time and the K
 // loop unrolls into straight-line code (a loop back-edge makes the compiler
 // wait for every load in flight at the loop head). NSTEPS == 0: runtime loop.
 template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS>
-__global__ __launch_bounds__(kStreamMaxWaves * 64, 3) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
+__global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
   typedef Elt<T> X;
   constexpr int NB = GATED ? 2 : 1;
   constexpr int VEC = X::VEC;
@@ -648,14 +685,12 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, 3) void k_paged_gemm_stream(G
   constexpr int RG = 64 / CG;                  // row groups per wavefront
   constexpr int RPL = kStreamK / RG;           // consecutive weight rows per lane
   constexpr int TN = BN / 16;
-  constexpr int KP = kStreamK + 16 / X::ES;    // LDS pitch (elements), 16 bytes of padding
+  constexpr int BNP = BN + X::B_PAD;           // row pitch of the wave's weight slice
   constexpr int SEG8 = X::SEG8;
-  constexpr int WORDS = RPL * X::ES / 4;       // packed 32-bit words per column
-  static_assert(CG * RG == 64 && RPL * RG == kStreamK && (WORDS == 1 || WORDS == 2 || WORDS % 4 == 0),
-                "stream tile shape");
-  static_assert(NB * 16 * BN * 4 <= NB * BN * KP * X::ES, "reduction must fit the wave buffer");
+  static_assert(CG * RG == 64 && RPL * RG == kStreamK, "stream tile shape");
+  static_assert(NB * 16 * BN * 4 <= NB * kStreamK * BNP * X::ES, "reduction must fit the wave buffer");
 
-  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves][NB * BN * KP];
+  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves][NB * kStreamK * BNP];
   extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
 
   const int nN = a.N / BN;
@@ -737,32 +772,12 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, 3) void k_paged_gemm_stream(G
   // Multiply step data into the accumulators; live == false (a step past the
   // end) multiplies by a zero A operand, which adds exact zeros.
   auto consume = [&](const u32x4 (&br)[NB][RPL], const u32x4 (&ar)[SEG8], bool live) {
-    // transpose: column c of the lane's segments gets RPL consecutive K values
+    // the wave's weight slice, row-major as it sits in the pool
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        uint32_t w[WORDS];
-        if constexpr (X::ES == 2) {
-#pragma unroll
-          for (int i = 0; i < WORDS; ++i)
-            w[i] = X::get(br[b][2 * i], c) | (X::get(br[b][2 * i + 1], c) << 16);
-        } else {
-#pragma unroll
-          for (int i = 0; i < WORDS; ++i) w[i] = X::get(br[b][i], c);
-        }
-        T* dst = wbuf + b * BN * KP + (cg * VEC + c) * KP + rg * RPL;
-        if constexpr (WORDS == 1) {
-          *reinterpret_cast<uint32_t*>(dst) = w[0];
-        } else if constexpr (WORDS == 2) {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-        } else {
-#pragma unroll
-          for (int i = 0; i < WORDS; i += 4)
-            *reinterpret_cast<u32x4*>(dst + i * 4 / X::ES) = u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]};
-        }
-      }
-    }
+      for (int j = 0; j < RPL; ++j)
+        *reinterpret_cast<u32x4*>(wbuf + b * kStreamK * BNP + (rg * RPL + j) * BNP + cg * VEC) = br[b][j];
     const bool use = live && a_ok;
     u32x4 af[SEG8];
 #pragma unroll
@@ -772,9 +787,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, 3) void k_paged_gemm_stream(G
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         u32x4 bf[SEG8];
-        const T* src = wbuf + b * BN * KP + (j * 16 + fi) * KP + fq * 8;
-#pragma unroll
-        for (int u = 0; u < SEG8; ++u) bf[u] = *reinterpret_cast<const u32x4*>(src + u * VEC);
+        X::bfrag16(wbuf + b * kStreamK * BNP, BNP, 0, j * 16, lane, bf);
         acc[b][j] = X::mma8(af, bf, acc[b][j]);
       }
     }
@@ -1028,10 +1041,13 @@ hipError_t launch_plan(Plan p, const GemmArgs& g, uint64_t tiles_max, hipStream_
   const bool wide = g.N % 128 == 0;
   switch (p.id) {
     case kPlan16:
-      if constexpr (GATED) return launch_stream<T, 64, 3, true>(g, tiles_max, st);
-      else
-        return wide ? launch_stream<T, 128, 3, false>(g, tiles_max, st)
-                    : launch_stream<T, 64, 3, false>(g, tiles_max, st);
+      if constexpr (GATED) {
+        if (g.N % kStreamUpBN == 0) return launch_stream<T, kStreamUpBN, kStreamUpDepth, true>(g, tiles_max, st);
+        return launch_stream<T, 64, 3, true>(g, tiles_max, st);
+      } else {
+        if (g.N % kStreamDnBN == 0) return launch_stream<T, kStreamDnBN, kStreamDnDepth, false>(g, tiles_max, st);
+        return launch_stream<T, 64, 3, false>(g, tiles_max, st);
+      }
     case kPlan64:
       if constexpr (!kF32) {
         constexpr TileShape t = GATED ? kT64Up : kT64Dn;
