@@ -352,15 +352,27 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
 
 constexpr int kSortChunk = 64;  // consecutive slots per thread per round (16 x 16-byte loads)
 
+// counts == nullptr: the workgroup builds the per-expert histogram itself in
+// LDS (small batches: this saves the separate count launch).
+constexpr int kSortSelfCountMax = 4096;   // routed slots
+
 __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
                                                     int BM, const int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ sorted_ids,
                                                     int32_t* __restrict__ expert_off,
                                                     int32_t* __restrict__ tile_expert) {
   __shared__ int sh[4];
+  __shared__ int hist[kMaxE];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const uint32_t ue = static_cast<uint32_t>(e);
+  if (counts == nullptr) {
+    for (int i = tid; i < E; i += 256) hist[i] = 0;
+    __syncthreads();
+    for (int f = tid; f < TK; f += 256) atomicAdd(&hist[ids[f]], 1);
+    __syncthreads();
+    counts = hist;
+  }
   // start of this expert's padded segment, and the padded total
   int before = 0, total = 0;
   for (int e2 = tid; e2 < E; e2 += 256) {
@@ -1089,11 +1101,14 @@ hipError_t launch_layer(const rimuru_moe_args* a, Plan p, const Layout& lay, hip
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if ((err = mark(1)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, st, a->topk_ids, TK, counts);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const bool self_count = TK <= kSortSelfCountMax;
+  if (!self_count) {
+    hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, st, a->topk_ids, TK, counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if ((err = mark(2)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_sort_align, dim3(E), dim3(256), 0, st, a->topk_ids, TK, E, p.bm, counts,
-                     a->sorted_ids, a->expert_off, tile_expert);
+  hipLaunchKernelGGL(k_sort_align, dim3(E), dim3(256), 0, st, a->topk_ids, TK, E, p.bm,
+                     self_count ? nullptr : counts, a->sorted_ids, a->expert_off, tile_expert);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   GemmArgs g{};
