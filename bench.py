@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="before every timed step, read this many MiB of scratch (evicts the "
+                         "Infinity Cache with clean lines); steps are then timed by an event pair each")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -134,12 +137,30 @@ def main():
 
     # Timed region 1: the headline. Stage events are left out here because
     # each event record costs the stream a few microseconds.
+    flush_buf = None
+    if args.flush_mib:
+        flush_buf = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device=dev)
+        flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+        pairs = [(R.event_create(), R.event_create()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step()
+        if flush_buf is not None:
+            torch.sum(flush_buf, dim=0, out=flush_sink)     # a read of the whole buffer
+            R.event_record(pairs[s][0])
+            step()
+            R.event_record(pairs[s][1])
+        else:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if flush_buf is not None:
+        # cache-cold steps: the step time is the event-pair time, not the wall
+        step_ms = [R.event_elapsed_ms(a, b) for a, b in pairs]
+        wall = sum(step_ms) / 1e3
+        for a, b in pairs:
+            R.event_destroy(a)
+            R.event_destroy(b)
     # Timed region 2: the same steps with an event before and after every
     # stage, on the stream the kernels run on, for per-kernel durations.
     evs = [[R.event_create() for _ in range(R.MOE_STAGES + 1)] for _ in range(args.steps)]
@@ -216,7 +237,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I,
                    "page_bytes": cfg.page_bytes, "pool_bytes": cfg.pool_bytes,
-                   "experts_touched": touched, "block_m": bufs.block_m},
+                   "experts_touched": touched, "block_m": bufs.block_m,
+                   "cache_flush_mib": args.flush_mib},
         "layer": {"tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
                   "hbm_gbs": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9, 1),
                   "algorithmic_bytes": w_bytes + io_bytes, "algorithmic_flops": flops,
