@@ -23,7 +23,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "paged_moe_expert_amd", "csrc", "moe_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_moe_expert_amd", "csrc")
+# sources each GEMM kernel is compiled from: a traffic measurement stays valid
+# while these are unchanged
+KERNEL_SOURCES = {"stream": ("moe_common.h", "moe_gemm_stream.hip"),
+                  "tiled": ("moe_common.h", "moe_gemm_tiled.hip")}
 STAGES = ["gating", "count", "sort", "gemm_up", "gemm_down", "combine"]
 
 
@@ -31,18 +35,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+def kernel_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
-def traffic_from_profiles(workload: str, kernel: str):
+def traffic_from_profiles(workload: str, kernel: str, kind: str):
     """HBM bytes per launch measured by rocprofv3 counters, if the committed
-    measurement was taken on the current kernel source; else None."""
+    measurement was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_source_sha256") != kernel_sha():
+    if d.get("kernel_source_sha256") != kernel_sha(kind):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -209,17 +216,18 @@ def main():
     mean = stage_ms.mean(axis=0)
     up_ms = float(mean[3])
     decode_like = (w_bytes + io_bytes) / HBM_PEAK_GBS > flops / (BF16_PEAK_TFLOPS * 1e3)
+    kind = "stream" if bufs.block_m == 16 else "tiled"
     if decode_like:
         achieved = up_bytes / (up_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "gemm_up", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(cfg.name, "gemm_up"),
+                "traffic": traffic_from_profiles(cfg.name, "gemm_up", kind),
                 "algorithmic_bytes_per_launch": up_bytes, "avg_launch_us": round(up_ms * 1e3, 2)}
     else:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "gemm_up", "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles(cfg.name, "gemm_up"),
+                "traffic": traffic_from_profiles(cfg.name, "gemm_up", kind),
                 "algorithmic_flops_per_launch": up_flops, "avg_launch_us": round(up_ms * 1e3, 2)}
 
     out = {

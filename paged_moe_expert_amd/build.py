@@ -11,12 +11,14 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "librimuru.so")
-SOURCES = [os.path.join(HERE, "csrc", "allocator.cpp"),
-           os.path.join(HERE, "csrc", "moe_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in
+           ("allocator.cpp", "moe_routing.hip", "moe_gemm_stream.hip", "moe_gemm_tiled.hip",
+            "moe_layer.hip")]
 ARCH = "gfx950"
 
 
@@ -28,7 +30,7 @@ def hipcc() -> str:
 
 
 def flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Wall", "-Wno-unused-function",
             # packed fp32 VALU forms stay off: plain fp32 code only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,18 +38,30 @@ def flags():
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile the library to `out`; defines are extra -D macros (tile tuning)."""
-    tmp = out + ".tmp"
-    cmd = [hipcc()] + flags() + [f"-D{d}" for d in defines] + SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile the library to `out`; defines are extra -D macros (tile tuning).
+
+    Translation units compile in parallel to objects beside `out`, then link."""
+    dflags = [f"-D{d}" for d in defines]
     noise = "is not a recognized feature for this target"
-    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
-    if verbose and msg.strip():
-        print(msg)
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
+        if verbose and msg.strip():
+            print(msg)
+
+    objdir = out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda so: run([hipcc()] + flags() + dflags + ["-c", so[0], "-o", so[1]]),
+                    zip(SOURCES, objs)))
+    tmp = out + ".tmp"
+    run([hipcc()] + flags() + ["-shared"] + objs + ["-o", tmp])
     os.replace(tmp, out)
     return out
 

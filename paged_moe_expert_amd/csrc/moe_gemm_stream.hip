@@ -1,0 +1,303 @@
+// Stages 4 and 5 of the fused MoE layer for few routed rows per expert
+// (decode): the grouped GEMM is a stream of expert weights read page by page
+// through the expert view's page table (Rimuru paper summary, abstract and
+// Figure 11, "Discrete FusedMoE"; Table 1 for the projections).
+#include <algorithm>
+
+#include "moe_common.h"
+
+namespace rimuru {
+
+// ---------------------------------------------------------------- stages 4, 5 for few rows: weight streaming
+
+// Few routed rows per expert: the GEMM is a weight stream. A workgroup owns
+// one 16-row tile and BN columns; its ksplit wavefronts each own a
+// contiguous K range and stream their weight rows with DEPTH steps of loads
+// in flight. Each step a wavefront transposes its own 32 x BN weight slice
+// through a private LDS buffer (LDS operations of one wavefront complete in
+// issue order, so no barrier is needed) and runs the MFMAs; the A operand is
+// loaded straight into registers. The ksplit partial sums are added in fixed
+// wavefront order at the end, so results are deterministic.
+constexpr int kStreamMaxWaves = 4;
+constexpr int kStreamK = 32;      // K rows per wavefront step
+// column-tile width and steps in flight of the gate/up and down streams
+// (compile-time overridable for tuning sweeps), and workgroups per CU
+#ifndef RIMURU_STREAM_UP
+#define RIMURU_STREAM_UP 128, 2
+#endif
+#ifndef RIMURU_STREAM_DN
+#define RIMURU_STREAM_DN 256, 2
+#endif
+#ifndef RIMURU_STREAM_WG_PER_CU
+#define RIMURU_STREAM_WG_PER_CU 2
+#endif
+#ifndef RIMURU_STREAM_WAVES
+#define RIMURU_STREAM_WAVES 4, 4
+#endif
+struct StreamWaves { int up, dn; };
+constexpr StreamWaves kStreamWaves{RIMURU_STREAM_WAVES};
+constexpr int kStreamUpWaves = kStreamWaves.up, kStreamDnWaves = kStreamWaves.dn;
+#ifndef RIMURU_STREAM_NARROW
+#define RIMURU_STREAM_NARROW 160, 32, 64
+#endif
+// Few experts touched: narrow the column tile (down to the given widths) while
+// fewer than min_groups workgroups would stream. Measured cache-cold on the
+// 2048x768 bf16 experts: one token (8 experts) streams gate/up 1.9x faster with
+// 32-column tiles, while at 28 experts 168 workgroups of 128 columns beat 336
+// of 64 (wider rows per page keep HBM bursts long), hence the low threshold.
+struct StreamNarrow { int64_t min_groups; int up_bn, dn_bn; };
+constexpr StreamNarrow kStreamNarrow{RIMURU_STREAM_NARROW};
+struct StreamShape { int bn, depth; };
+constexpr StreamShape kStreamUp{RIMURU_STREAM_UP}, kStreamDn{RIMURU_STREAM_DN};
+constexpr int kStreamUpBN = kStreamUp.bn, kStreamUpDepth = kStreamUp.depth;
+constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
+
+// NSTEPS > 0: the wavefront's step count is known at compile time and the K
+// loop unrolls into straight-line code (a loop back-edge makes the compiler
+// wait for every load in flight at the loop head). NSTEPS == 0: runtime loop.
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS>
+__global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
+  typedef Elt<T> X;
+  constexpr int NB = GATED ? 2 : 1;
+  constexpr int VEC = X::VEC;
+  constexpr int CG = BN / VEC;                 // 16-byte column groups per weight row
+  constexpr int RG = 64 / CG;                  // row groups per wavefront
+  constexpr int RPL = kStreamK / RG;           // consecutive weight rows per lane
+  constexpr int TN = BN / 16;
+  constexpr int BNP = BN + X::B_PAD;           // row pitch of the wave's weight slice
+  constexpr int SEG8 = X::SEG8;
+  static_assert(CG * RG == 64 && RPL * RG == kStreamK, "stream tile shape");
+  static_assert(NB * 16 * BN * 4 <= NB * kStreamK * BNP * X::ES, "reduction must fit the wave buffer");
+
+  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves][NB * kStreamK * BNP];
+  extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
+
+  const int nN = a.N / BN;
+  const int n_tiles = a.expert_off[a.E] / 16;
+  const int L = n_tiles * nN;
+  const int chunk = (L + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  if (idx >= chunk) return;
+  const int logical = xcd * chunk + idx;
+  if (logical >= L) return;
+  const int mt = logical / nN;
+  const int nt = logical - mt * nN;
+  const int e = a.tile_expert[mt];
+  const int r0 = mt * 16;
+  const int n0 = nt * BN;
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int fi = lane & 15, fq = lane >> 4;
+  const int kw = a.K / ksplit;
+  const int nsteps = kw / kStreamK;
+  const int kbase = wv * kw;
+
+  // A operand: row fi of the tile, K values fq*8 .. fq*8+7 of each step.
+  // Padding rows read a valid row and are zeroed by a select, so the main
+  // loop has no branch around a load (a branch there makes the compiler wait
+  // for every load in flight at the join).
+  const T* arow;
+  bool a_ok = true;
+  if (a.kdiv > 0) {
+    const int slot = a.sorted_ids[r0 + fi];
+    a_ok = slot < a.TK;
+    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(a_ok ? slot / a.kdiv : 0) * a.lda;
+  } else {
+    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r0 + fi) * a.lda;
+  }
+  const int cg = lane % CG, rg = lane / CG;
+  // Page lookups read LDS: a global load here would make every weight load
+  // wait for all older ones (vector-memory loads retire in order).
+  for (int i = threadIdx.x; i < NB * a.P; i += blockDim.x) {
+    const int b = i / a.P, q = i - b * a.P;
+    pt_lds[i] = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
+  }
+  __syncthreads();
+  const int32_t* pt_row[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) pt_row[b] = pt_lds + b * a.P;
+  const uint32_t col_bytes = static_cast<uint32_t>(n0 + cg * VEC) * X::ES;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
+
+  u32x4 breg[DEPTH][NB][RPL];
+  u32x4 areg[DEPTH][SEG8];
+  f32x4 acc[NB][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  T* wbuf = lds[wv];
+
+  // Loads of step st (clamped to the last step: the surplus loads at the end
+  // repeat addresses already in cache and their data is never used).
+  auto issue = [&](u32x4 (&br)[NB][RPL], u32x4 (&ar)[SEG8], int st) {
+    st = min(st, nsteps - 1);
+    const int k0 = kbase + st * kStreamK;
+#pragma unroll
+    for (int u = 0; u < SEG8; ++u) ar[u] = *reinterpret_cast<const u32x4*>(arow + k0 + fq * 8 + u * VEC);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) {
+        const uint32_t f = static_cast<uint32_t>(k0 + rg * RPL + j) * row_bytes + col_bytes;
+        const uint32_t q = page_index(f, a.pd);
+        const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+        br[b][j] = *reinterpret_cast<const u32x4*>(p);
+      }
+    }
+  };
+
+  // Multiply step data into the accumulators; live == false (a step past the
+  // end) multiplies by a zero A operand, which adds exact zeros.
+  auto consume = [&](const u32x4 (&br)[NB][RPL], const u32x4 (&ar)[SEG8], bool live) {
+    // the wave's weight slice, row-major as it sits in the pool
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < RPL; ++j)
+        *reinterpret_cast<u32x4*>(wbuf + b * kStreamK * BNP + (rg * RPL + j) * BNP + cg * VEC) = br[b][j];
+    const bool use = live && a_ok;
+    u32x4 af[SEG8];
+#pragma unroll
+    for (int u = 0; u < SEG8; ++u) af[u] = use ? ar[u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 bf[SEG8];
+        X::bfrag16(wbuf + b * kStreamK * BNP, BNP, 0, j * 16, lane, bf);
+        acc[b][j] = X::mma8(af, bf, acc[b][j]);
+      }
+    }
+  };
+
+  if constexpr (NSTEPS > 0) {
+    // Straight-line pipeline: DEPTH - 1 steps in flight ahead of the one consumed.
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (d < NSTEPS) issue(breg[d], areg[d], d);
+#pragma unroll
+    for (int st = 0; st < NSTEPS; ++st) {
+      if (st + DEPTH - 1 < NSTEPS)
+        issue(breg[(st + DEPTH - 1) % DEPTH], areg[(st + DEPTH - 1) % DEPTH], st + DEPTH - 1);
+      consume(breg[st % DEPTH], areg[st % DEPTH], true);
+    }
+  } else {
+    // Branch-free loop: DEPTH - 1 steps in flight ahead of the one consumed.
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) issue(breg[d], areg[d], d);
+    for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        issue(breg[(d + DEPTH - 1) % DEPTH], areg[(d + DEPTH - 1) % DEPTH], s0 + d + DEPTH - 1);
+        consume(breg[d], areg[d], s0 + d < nsteps);
+      }
+    }
+  }
+
+  // ---- reduce the ksplit partial sums in wavefront order, then the epilogue
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(wbuf);           // [NB][16][BN] of this wavefront
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(b * 16 + 4 * fq + r) * BN + j * 16 + fi] = acc[b][j][r];
+  __syncthreads();
+  constexpr int PER = 4;                                  // outputs per thread per pass
+  T* C = reinterpret_cast<T*>(a.C);
+  for (int o = threadIdx.x * PER; o < 16 * BN; o += blockDim.x * PER) {
+    const int row = o / BN, col = o % BN;
+    float v[NB][PER];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < PER; ++c) v[b][c] = 0.0f;
+    for (int w = 0; w < ksplit; ++w) {
+      const float* rw = reinterpret_cast<const float*>(lds[w]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < PER; ++c) v[b][c] += rw[(b * 16 + row) * BN + col + c];
+    }
+    if constexpr (GATED) {
+      T* dst = C + static_cast<int64_t>(r0 + row) * a.ldc + n0 + col;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) X::put(dst + c, silu(v[0][c]) * v[1][c]);
+    } else {
+      const int slot = a.sorted_ids[r0 + row];
+      if (slot < a.TK) {
+        const float wt = a.topk_w[slot];
+        T* dst = C + static_cast<int64_t>(slot) * a.ldc + n0 + col;
+#pragma unroll
+        for (int c = 0; c < PER; ++c) X::put(dst + c, wt * v[0][c]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+namespace {
+
+template <typename T, int BN, int DEPTH, bool GATED>
+hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  const int ksteps = g.K / kStreamK;
+  const int max_split = GATED ? kStreamUpWaves : kStreamDnWaves;
+  const int ksplit = (ksteps % 4 == 0 && max_split >= 4) ? 4 : (ksteps % 2 == 0 && max_split >= 2) ? 2 : 1;
+  if (g.N % BN != 0 || g.K % kStreamK != 0) return hipErrorInvalidValue;
+  uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
+  uint64_t grid = (blocks + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  const dim3 gd(static_cast<uint32_t>(grid)), bd(ksplit * 64);
+  const size_t pt_bytes = static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
+  switch (ksteps / ksplit) {
+#define RIMURU_STREAM_CASE(n) \
+    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n>), gd, bd, pt_bytes, st, g, ksplit); break;
+    RIMURU_STREAM_CASE(2)
+    RIMURU_STREAM_CASE(3)
+    RIMURU_STREAM_CASE(4)
+    RIMURU_STREAM_CASE(6)
+    RIMURU_STREAM_CASE(8)
+    RIMURU_STREAM_CASE(12)
+    RIMURU_STREAM_CASE(16)
+#undef RIMURU_STREAM_CASE
+    // other step counts: runtime loop, one step less in flight (register budget)
+    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0>), gd, bd, pt_bytes, st, g, ksplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T, bool GATED>
+hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {
+    return launch_stream<T, 64, 3, GATED>(g, tiles_max, st);
+  } else {
+    // Widest column tile that still yields enough workgroups to keep every
+    // CU streaming when only a few experts are touched.
+    const int64_t touched = std::min<int64_t>(g.E, g.TK);
+    auto enough = [&](int bn, int floor_bn) {
+      return g.N % bn == 0 && (bn <= floor_bn || touched * (g.N / bn) >= kStreamNarrow.min_groups);
+    };
+    if constexpr (GATED) {
+      if (enough(kStreamUpBN, kStreamNarrow.up_bn)) return launch_stream<T, kStreamUpBN, kStreamUpDepth, true>(g, tiles_max, st);
+      if (enough(64, kStreamNarrow.up_bn)) return launch_stream<T, 64, 3, true>(g, tiles_max, st);
+      return launch_stream<T, 32, 3, true>(g, tiles_max, st);
+    } else {
+      if (enough(kStreamDnBN, kStreamNarrow.dn_bn)) return launch_stream<T, kStreamDnBN, kStreamDnDepth, false>(g, tiles_max, st);
+      if (enough(128, kStreamNarrow.dn_bn)) return launch_stream<T, 128, 3, false>(g, tiles_max, st);
+      return launch_stream<T, 64, 3, false>(g, tiles_max, st);
+    }
+  }
+}
+
+template hipError_t launch_streamed<uint16_t, true>(const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<uint16_t, false>(const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<float, true>(const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<float, false>(const GemmArgs&, uint64_t, hipStream_t);
+
+}  // namespace rimuru

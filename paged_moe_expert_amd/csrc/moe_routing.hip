@@ -1,0 +1,349 @@
+// Routing stages of the fused MoE layer and the combine, plus the page-wise
+// weight store. Not on the pages: gating, sort and combine follow the plain
+// readings stated in the oracle (softmax over the kept top-k logits, stable
+// expert grouping padded to the tile height, rank-ordered fp32 sum).
+//
+//   gating   one wavefront per token: top-k on raw logits, then softmax over
+//            the kept logits (the renormalised softmax weights)
+//   count    one workgroup per expert: routed slots per expert
+//   sort     one workgroup per expert: stable list of slots t*k+j, padded to
+//            the tile height, tile -> expert map
+//   combine  y[t] = sum_j y_slot[t*k+j], j in rank order
+#include "moe_common.h"
+
+namespace rimuru {
+
+// ---------------------------------------------------------------- stage 1: gating
+
+// Total order on (logit, expert): larger logit first, then lower index;
+// -0 and +0 compare equal. Logits are finite (precondition).
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  uint32_t s = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(s) << 32) | (0xffffffffu - e);
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  uint32_t s = static_cast<uint32_t>(key >> 32);
+  uint32_t u = (s & 0x80000000u) ? (s & 0x7fffffffu) : ~s;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Top-k of one token's logits by one wavefront. Lane r < k ends with the
+// r-th expert (rank order) in *e_out and its logit in *l_out; every lane gets
+// the weight denominator's terms in rank order via the returned softmax value.
+template <int EPL>
+__device__ __forceinline__ void load_logits(const float* row, int E, int lane, float (&v)[EPL]) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < E) ? row[e] : 0.0f;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void select_topk_vals(const float (&v)[EPL], int E, int k, int lane,
+                                                 uint32_t* e_out, float* w_out) {
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    key[i] = (e < E) ? rank_key(v[i], static_cast<uint32_t>(e)) : 0ull;
+  }
+  uint32_t my_e = 0;
+  float my_l = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    uint32_t e = 0xffffffffu - static_cast<uint32_t>(best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (static_cast<uint32_t>(lane + 64 * i) == e) key[i] = 0ull;
+    if (lane == r) {
+      my_e = e;
+      my_l = key_logit(best);
+    }
+  }
+  // softmax over the kept logits = renormalised full softmax; the sum runs
+  // over the kept experts in rank order
+  const float m = __shfl(my_l, 0, 64);
+  const float ex = (lane < k) ? expf(my_l - m) : 0.0f;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += __shfl(ex, j, 64);
+  *e_out = my_e;
+  *w_out = ex / s;
+}
+
+template <int EPL>
+__device__ __forceinline__ void select_topk(const float* row, int E, int k, int lane,
+                                            uint32_t* e_out, float* w_out) {
+  float v[EPL];
+  load_logits<EPL>(row, E, lane, v);
+  select_topk_vals<EPL>(v, E, k, lane, e_out, w_out);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits, int T, int E,
+                                                int k, int32_t* __restrict__ ids,
+                                                float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  uint32_t e;
+  float wt;
+  select_topk<EPL>(logits + static_cast<int64_t>(t) * E, E, k, lane, &e, &wt);
+  if (lane < k) {
+    ids[static_cast<int64_t>(t) * k + lane] = static_cast<int32_t>(e);
+    w[static_cast<int64_t>(t) * k + lane] = wt;
+  }
+}
+
+// ---------------------------------------------------------------- stage 2: count
+
+// ids is 16-byte aligned (validated); 8 independent 16-byte loads per thread
+// are in flight per round.
+__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int TK,
+                                               int32_t* __restrict__ counts) {
+  __shared__ int part[4];
+  const int e = blockIdx.x;
+  const int n4 = TK >> 2;
+  const u32x4* v = reinterpret_cast<const u32x4*>(ids);
+  const uint32_t ue = static_cast<uint32_t>(e);
+  int c = 0;
+  for (int base = 0; base < n4; base += 256 * 8) {
+    u32x4 r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 256 + threadIdx.x;
+      r[u] = (i < n4) ? v[i] : u32x4{~0u, ~0u, ~0u, ~0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      c += (r[u][0] == ue) + (r[u][1] == ue) + (r[u][2] == ue) + (r[u][3] == ue);
+  }
+  for (int f = n4 * 4 + threadIdx.x; f < TK; f += 256) c += (ids[f] == e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[e] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ---------------------------------------------------------------- stage 3: sort + align
+
+// Exclusive prefix of v over the 256 threads of the block; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sh[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += (i < wv) ? sh[i] : 0;
+    all += sh[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+constexpr int kSortChunk = 64;  // consecutive slots per thread per round (16 x 16-byte loads)
+
+// counts == nullptr: the workgroup builds the per-expert histogram itself in
+// LDS (small batches: this saves the separate count launch).
+constexpr int kSortSelfCountMax = 4096;   // routed slots
+
+__global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
+                                                    int BM, const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ sorted_ids,
+                                                    int32_t* __restrict__ expert_off,
+                                                    int32_t* __restrict__ tile_expert) {
+  __shared__ int sh[4];
+  __shared__ int hist[kMaxE];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t ue = static_cast<uint32_t>(e);
+  if (counts == nullptr) {
+    for (int i = tid; i < E; i += 256) hist[i] = 0;
+    __syncthreads();
+    for (int f = tid; f < TK; f += 256) atomicAdd(&hist[ids[f]], 1);
+    __syncthreads();
+    counts = hist;
+  }
+  // start of this expert's padded segment, and the padded total
+  int before = 0, total = 0;
+  for (int e2 = tid; e2 < E; e2 += 256) {
+    int pc = (counts[e2] + BM - 1) / BM * BM;
+    total += pc;
+    before += (e2 < e) ? pc : 0;
+  }
+  int sum_before, sum_total;
+  block_excl_scan(before, &sum_before, sh);   // block sums of the per-thread partials
+  block_excl_scan(total, &sum_total, sh);
+  const int seg = sum_before;
+  const int cnt = counts[e];
+  if (tid == 0) {
+    expert_off[e] = seg;
+    if (e == 0) expert_off[E] = sum_total;
+  }
+  const bool vec = (TK & 3) == 0;
+  int running = 0;
+  for (int base = 0; base < TK; base += 256 * kSortChunk) {
+    const int f0 = base + tid * kSortChunk;
+    uint64_t mask = 0;
+    if (vec) {
+      u32x4 r[kSortChunk / 4];
+#pragma unroll
+      for (int u = 0; u < kSortChunk / 4; ++u)
+        r[u] = (f0 + 4 * u < TK) ? *reinterpret_cast<const u32x4*>(ids + f0 + 4 * u)
+                                 : u32x4{~0u, ~0u, ~0u, ~0u};
+#pragma unroll
+      for (int u = 0; u < kSortChunk / 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mask |= static_cast<uint64_t>(r[u][c] == ue) << (4 * u + c);
+    } else {
+      for (int i = 0; i < kSortChunk; ++i) {
+        const int f = f0 + i;
+        if (f < TK && ids[f] == e) mask |= 1ull << i;
+      }
+    }
+    int chunk_total;
+    int pos = seg + running + block_excl_scan(__popcll(mask), &chunk_total, sh);
+    while (mask) {
+      const int i = __ffsll(static_cast<long long>(mask)) - 1;
+      sorted_ids[pos++] = f0 + i;
+      mask &= mask - 1;
+    }
+    running += chunk_total;
+  }
+  const int padded = (cnt + BM - 1) / BM * BM;
+  for (int i = cnt + tid; i < padded; i += 256) sorted_ids[seg + i] = TK;
+  for (int i = tid; i < padded / BM; i += 256) tile_expert[seg / BM + i] = e;
+}
+
+// ---------------------------------------------------------------- stage 6: combine
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ yslot, int k, int H,
+                                                 T* __restrict__ y) {
+  typedef Elt<T> X;
+  constexpr int VEC = X::VEC;
+  const int t = blockIdx.x;
+  const int h0 = (blockIdx.y * 256 + threadIdx.x) * VEC;
+  if (h0 >= H) return;
+  float acc[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) acc[c] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    u32x4 s = *reinterpret_cast<const u32x4*>(yslot + (static_cast<int64_t>(t) * k + j) * H + h0);
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] += X::to_f32(X::get(s, c));
+  }
+  u32x4 o;
+  if constexpr (X::ES == 2) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = X::from_f32(acc[2 * c]) | (X::from_f32(acc[2 * c + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = X::from_f32(acc[c]);
+  }
+  *reinterpret_cast<u32x4*>(y + static_cast<int64_t>(t) * H + h0) = o;
+}
+
+// ---------------------------------------------------------------- weight loading
+
+__global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool,
+                                                     const int32_t* __restrict__ pt, int P,
+                                                     PageDiv pd, const uint8_t* __restrict__ src,
+                                                     uint64_t proj_bytes, uint64_t n_segs) {
+  for (uint64_t s = blockIdx.x * 256ull + threadIdx.x; s < n_segs; s += gridDim.x * 256ull) {
+    uint64_t byte = s * 16;
+    uint64_t proj = byte / proj_bytes;
+    uint32_t off = static_cast<uint32_t>(byte - proj * proj_bytes);
+    uint32_t q = page_index(off, pd);
+    uint8_t* dst = pool + static_cast<uint64_t>(pt[proj * P + q]) * pd.page + (off - q * pd.page);
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + byte);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+PageDiv make_div(uint32_t page) {
+  uint32_t l = 0;
+  while ((1ull << l) < page) ++l;
+  unsigned __int128 num = (static_cast<unsigned __int128>(1) << 32) * ((1ull << l) - page);
+  uint64_t m = static_cast<uint64_t>(num / page) + 1 + (1ull << 32);
+  return PageDiv{m, 32 + l, page};
+}
+
+hipError_t launch_routing(const float* logits, int T, int E, int k, int bm, int32_t* topk_ids,
+                          float* topk_w, int32_t* counts, int32_t* sorted_ids, int32_t* expert_off,
+                          int32_t* tile_expert, hipEvent_t* ev, hipStream_t st) {
+  hipError_t err;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+  const int TK = T * k;
+  const int epl = (E + 63) / 64;
+  const dim3 grid((T + 3) / 4);
+  if (epl <= 1) hipLaunchKernelGGL(k_gating<1>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);
+  else if (epl <= 2) hipLaunchKernelGGL(k_gating<2>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);
+  else if (epl <= 4) hipLaunchKernelGGL(k_gating<4>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);
+  else hipLaunchKernelGGL(k_gating<8>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = mark(1)) != hipSuccess) return err;
+  const bool self_count = TK <= kSortSelfCountMax;
+  if (!self_count) {
+    hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, st, topk_ids, TK, counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if ((err = mark(2)) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_sort_align, dim3(E), dim3(256), 0, st, topk_ids, TK, E, bm,
+                     self_count ? nullptr : counts, sorted_ids, expert_off, tile_expert);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_combine(const T* yslot, int T_, int k, int H, T* y, hipStream_t st) {
+  constexpr int VEC = Elt<T>::VEC;
+  const dim3 grid(T_, (H + 256 * VEC - 1) / (256 * VEC));
+  hipLaunchKernelGGL(k_combine<T>, grid, dim3(256), 0, st, yslot, k, H, y);
+  return hipGetLastError();
+}
+template hipError_t launch_combine<uint16_t>(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
+template hipError_t launch_combine<float>(const float*, int, int, int, float*, hipStream_t);
+
+hipError_t launch_store_pages(uint8_t* pool, const int32_t* pt, int P, uint32_t page_bytes,
+                              const uint8_t* src, uint64_t proj_bytes, uint64_t n_segs, hipStream_t st) {
+  uint64_t blocks = (n_segs + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_store_pages, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, pool, pt, P,
+                     make_div(page_bytes), src, proj_bytes, n_segs);
+  return hipGetLastError();
+}
+
+}  // namespace rimuru
