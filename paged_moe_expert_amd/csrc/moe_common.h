@@ -58,6 +58,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
+// Two fp32 values -> packed bf16 pair (lo in bits 15:0), round to nearest even,
+// by the hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Value of lane l ^ 1 (a DPP quad permutation, no LDS traffic).
+__device__ __forceinline__ float swap_lane_pair(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------- elements
 
 template <typename T>

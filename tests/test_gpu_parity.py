@@ -85,6 +85,10 @@ CUSTOM = [
     # 24576 pages per projection: too many to stage in LDS, read from global
     ("bf16-huge-page-table", 2, 1, 2048, 768, 300, "bf16", 128, None),
     ("bf16-huge-page-table-decode", 2, 1, 2048, 768, 8, "bf16", 128, None),
+    # 128-row plan with 256-column gate/up and 512-column down tiles
+    ("bf16-pipelined-tiles", 8, 2, 512, 256, 1200, "bf16", 4 * KIB, None),
+    ("bf16-pipelined-odd-page-skewed", 8, 2, 512, 512, 1500, "bf16", 12 * KIB, [3, 2, 1, 0, 0, 0, -1, -40]),
+    ("bf16-pipelined-many-experts", 32, 4, 512, 256, 1400, "bf16", 64 * KIB, None),
 ]
 
 
