@@ -55,7 +55,10 @@ constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
 // NSTEPS > 0: the wavefront's step count is known at compile time and the K
 // loop unrolls into straight-line code (a loop back-edge makes the compiler
 // wait for every load in flight at the loop head). NSTEPS == 0: runtime loop.
-template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS>
+// ONE_PAGE: each projection lies in a single page (P == 1), so a weight
+// segment's address is that page's address plus its offset; otherwise every
+// segment looks its page up.
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE>
 __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
   typedef Elt<T> X;
   constexpr int NB = GATED ? 2 : 1;
@@ -108,14 +111,21 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   const int cg = lane % CG, rg = lane / CG;
   // Page lookups read LDS: a global load here would make every weight load
   // wait for all older ones (vector-memory loads retire in order).
-  for (int i = threadIdx.x; i < NB * a.P; i += blockDim.x) {
-    const int b = i / a.P, q = i - b * a.P;
-    pt_lds[i] = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
-  }
-  __syncthreads();
   const int32_t* pt_row[NB];
+  const uint8_t* page0[NB];                    // ONE_PAGE: the projection's page
+  if constexpr (ONE_PAGE) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) pt_row[b] = pt_lds + b * a.P;
+    for (int b = 0; b < NB; ++b)
+      page0[b] = a.pool + static_cast<uint64_t>(static_cast<uint32_t>(a.pt[e * 3 + (GATED ? b : 2)])) * a.pd.page;
+  } else {
+    for (int i = threadIdx.x; i < NB * a.P; i += blockDim.x) {
+      const int b = i / a.P, q = i - b * a.P;
+      pt_lds[i] = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) pt_row[b] = pt_lds + b * a.P;
+  }
   const uint32_t col_bytes = static_cast<uint32_t>(n0 + cg * VEC) * X::ES;
   const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
 
@@ -141,8 +151,13 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
 #pragma unroll
       for (int j = 0; j < RPL; ++j) {
         const uint32_t f = static_cast<uint32_t>(k0 + rg * RPL + j) * row_bytes + col_bytes;
-        const uint32_t q = page_index(f, a.pd);
-        const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+        const uint8_t* p;
+        if constexpr (ONE_PAGE) {
+          p = page0[b] + f;
+        } else {
+          const uint32_t q = page_index(f, a.pd);
+          p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+        }
         br[b][j] = *reinterpret_cast<const u32x4*>(p);
       }
     }
@@ -242,6 +257,24 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
 
 namespace {
 
+template <typename T, int BN, int DEPTH, bool GATED, bool ONE_PAGE>
+void launch_stream_steps(int steps, dim3 gd, dim3 bd, size_t lds, hipStream_t st, const GemmArgs& g, int ksplit) {
+  switch (steps) {
+#define RIMURU_STREAM_CASE(n) \
+    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n, ONE_PAGE>), gd, bd, lds, st, g, ksplit); break;
+    RIMURU_STREAM_CASE(2)
+    RIMURU_STREAM_CASE(3)
+    RIMURU_STREAM_CASE(4)
+    RIMURU_STREAM_CASE(6)
+    RIMURU_STREAM_CASE(8)
+    RIMURU_STREAM_CASE(12)
+    RIMURU_STREAM_CASE(16)
+#undef RIMURU_STREAM_CASE
+    // other step counts: runtime loop, one step less in flight (register budget)
+    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0, ONE_PAGE>), gd, bd, lds, st, g, ksplit);
+  }
+}
+
 template <typename T, int BN, int DEPTH, bool GATED>
 hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   const int ksteps = g.K / kStreamK;
@@ -252,20 +285,11 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
   uint64_t grid = (blocks + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   const dim3 gd(static_cast<uint32_t>(grid)), bd(ksplit * 64);
-  const size_t pt_bytes = static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
-  switch (ksteps / ksplit) {
-#define RIMURU_STREAM_CASE(n) \
-    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n>), gd, bd, pt_bytes, st, g, ksplit); break;
-    RIMURU_STREAM_CASE(2)
-    RIMURU_STREAM_CASE(3)
-    RIMURU_STREAM_CASE(4)
-    RIMURU_STREAM_CASE(6)
-    RIMURU_STREAM_CASE(8)
-    RIMURU_STREAM_CASE(12)
-    RIMURU_STREAM_CASE(16)
-#undef RIMURU_STREAM_CASE
-    // other step counts: runtime loop, one step less in flight (register budget)
-    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0>), gd, bd, pt_bytes, st, g, ksplit);
+  if (g.P == 1) {
+    launch_stream_steps<T, BN, DEPTH, GATED, true>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
+  } else {
+    const size_t pt_bytes = static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
+    launch_stream_steps<T, BN, DEPTH, GATED, false>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
   }
   return hipGetLastError();
 }
