@@ -75,6 +75,67 @@ def cpu_baseline(cfg, xb, lg, wb, n_tokens: int):
                       f"page resolution included; {dt:.2f} s"}
 
 
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np):
+    """Upload n experts' weights from pinned host memory into fresh pages of
+    their own, first alone, then while the layer runs on the compute stream."""
+    n = min(args.upload_experts, cfg.E)
+    proj = cfg.proj_bytes
+    pages = n * 3 * cfg.P
+    dst = torch.empty(pages * cfg.page_bytes, dtype=torch.uint8, device=dev)
+    host = torch.from_numpy(np.ascontiguousarray(wb[:n]).view(np.uint8).reshape(n, 3, proj)).pin_memory()
+    rows = np.arange(pages, dtype=np.int32).reshape(n, 3, cfg.P)
+    side = torch.cuda.Stream(device=dev)
+    main = torch.cuda.current_stream(dev)
+
+    def upload_round():
+        for j in range(n):
+            R.expert_upload(dst, rows[j], cfg.page_bytes, host[j], stream=side)
+
+    upload_round()                                      # warm
+    side.synchronize()
+    e0, e1 = R.event_create(), R.event_create()
+    R.event_record(e0, side)
+    for _ in range(3):
+        upload_round()
+    R.event_record(e1, side)
+    alone_ms = R.event_elapsed_ms(e0, e1) / 3
+    bytes_round = n * 3 * proj
+    # overlapped: enough rounds to cover the timed layer steps
+    torch.cuda.synchronize()
+    m0, m1 = R.event_create(), R.event_create()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    rounds = max(1, int(round(layer_ms * args.steps / alone_ms)))
+    torch.cuda.synchronize()
+    R.event_record(e0, side)
+    R.event_record(m0, main)
+    for _ in range(rounds):
+        upload_round()
+    for _ in range(args.steps):
+        step()
+    R.event_record(e1, side)
+    R.event_record(m1, main)
+    torch.cuda.synchronize()
+    up_ms = R.event_elapsed_ms(e0, e1)
+    lay_ms = R.event_elapsed_ms(m0, m1) / args.steps
+    for e in (e0, e1, m0, m1):
+        R.event_destroy(e)
+    del dst
+    gbs_alone = bytes_round / (alone_ms * 1e-3) / 1e9
+    gbs_ovl = rounds * bytes_round / (up_ms * 1e-3) / 1e9
+    return {"experts": n, "bytes_per_round": bytes_round, "pages_per_expert": 3 * cfg.P,
+            "upload_gbs_alone": round(gbs_alone, 2), "upload_gbs_overlapped": round(gbs_ovl, 2),
+            "peak_gbs": PCIE_PEAK_GBS, "frac_alone": round(gbs_alone / PCIE_PEAK_GBS, 4),
+            "layer_ms_alone": round(layer_ms, 4), "layer_ms_overlapped": round(lay_ms, 4),
+            "rounds_overlapped": rounds}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +147,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--upload-experts", type=int, default=8,
+                    help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
+    ap.add_argument("--no-contiguous", action="store_true",
+                    help="skip the comparison run on a contiguous layout of the same weights")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="before every timed step, read this many MiB of scratch (evicts the "
                          "Infinity Cache with clean lines); steps are then timed by an event pair each")
@@ -148,26 +213,33 @@ def main():
     if args.flush_mib:
         flush_buf = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device=dev)
         flush_sink = torch.empty((), dtype=torch.float32, device=dev)
-        pairs = [(R.event_create(), R.event_create()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        if flush_buf is not None:
-            torch.sum(flush_buf, dim=0, out=flush_sink)     # a read of the whole buffer
-            R.event_record(pairs[s][0])
-            step()
-            R.event_record(pairs[s][1])
-        else:
-            step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if flush_buf is not None:
+
+    def timed(run):
+        """Seconds for args.steps calls of run(), and the per-step ms list
+        when every step is cache-cold (else None)."""
+        pairs = [(R.event_create(), R.event_create()) for _ in range(args.steps)] if flush_buf is not None else []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            if flush_buf is not None:
+                torch.sum(flush_buf, dim=0, out=flush_sink)     # a read of the whole buffer
+                R.event_record(pairs[s][0])
+                run()
+                R.event_record(pairs[s][1])
+            else:
+                run()
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        if not pairs:
+            return secs, None
         # cache-cold steps: the step time is the event-pair time, not the wall
-        step_ms = [R.event_elapsed_ms(a, b) for a, b in pairs]
-        wall = sum(step_ms) / 1e3
+        ms = [R.event_elapsed_ms(a, b) for a, b in pairs]
         for a, b in pairs:
             R.event_destroy(a)
             R.event_destroy(b)
+        return sum(ms) / 1e3, ms
+
+    wall, step_ms = timed(step)
     # Timed region 2: the same steps with an event before and after every
     # stage, on the stream the kernels run on, for per-kernel durations.
     evs = [[R.event_create() for _ in range(R.MOE_STAGES + 1)] for _ in range(args.steps)]
@@ -186,6 +258,34 @@ def main():
             R.event_destroy(e)
     log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms "
         f"({wall_events * 1e3:.2f} ms with stage events)")
+
+    # Timed region 3: the same layer on a contiguous layout of the same weights
+    # (pages consecutive and in order), for the cost of paging.
+    cont = None
+    if not args.no_contiguous:
+        from paged_moe_expert_amd.layouts import contiguous_page_table
+        cpt = torch.from_numpy(contiguous_page_table(cfg)).to(dev)
+        cpool = torch.empty(cfg.E * 3 * cfg.P * cfg.page_bytes, dtype=torch.uint8, device=dev)
+        wdev = torch.from_numpy(wb.view(idt)).to(dev)
+        R.experts_store(cpool, cpt, wdev, cfg.page_bytes)
+        del wdev
+        ybuf = bufs.y.clone()
+        R.fused_moe_paged(x, lgd, cpool, cpt, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ybuf.view(torch.uint8), bufs.y.view(torch.uint8)))
+        def cstep():
+            R.fused_moe_paged(x, lgd, cpool, cpt, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
+        for _ in range(args.warmup):
+            cstep()
+        cont_ms = timed(cstep)[0] * 1e3 / args.steps
+        del cpool
+        cont = {"ms_per_step": round(cont_ms, 4), "bitwise_equal_output": same}
+
+    # Timed region 4: dual-buffer expert upload (host -> fresh expert pages on a
+    # copy stream), alone and overlapped with the layer on the compute stream.
+    upload = None
+    if args.upload_experts:
+        upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -212,6 +312,11 @@ def main():
     up_flops = 4.0 * HI * TK
 
     ms_step = wall * 1e3 / args.steps
+    if step_ms is not None:
+        per_step, step_src = np.array(step_ms), "event pair around each cache-cold step"
+    else:
+        per_step = stage_ms.sum(axis=1)
+        step_src = "sum of the stage-event intervals of each step (event records included)"
     med = np.median(stage_ms, axis=0)
     mean = stage_ms.mean(axis=0)
     up_ms = float(mean[3])
@@ -252,9 +357,16 @@ def main():
                   "algorithmic_bytes": w_bytes + io_bytes, "algorithmic_flops": flops,
                   "hbm_frac": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "stages_us_median": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, med)},
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+        "step_ms_source": step_src,
         "ms_per_step_with_stage_events": round(wall_events * 1e3 / args.steps, 4),
         "roofline": roof,
     }
+    if upload is not None:
+        out["expert_upload"] = upload
+    if cont is not None:
+        cont["paged_over_contiguous_minus_1"] = round(ms_step / cont["ms_per_step"] - 1.0, 4)
+        out["contiguous"] = cont
     if not args.no_cpu:
         log("[bench] timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(cfg.with_T(T), xb, lg, wb, min(args.cpu_tokens, T))

@@ -249,6 +249,30 @@ rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt, int32_t E
                                    uint64_t page_bytes, const void* src, uint64_t proj_bytes,
                                    void* hip_stream);
 
+/* Elastic expert offloading, dual-buffer upload (Rimuru paper summary,
+ * Figure 8: expert prefetch overlapped with execution, no device-to-device
+ * copy): copy one expert's three projections from host memory straight into
+ * fresh expert-view pages, one host-to-device copy per page, on hip_stream
+ * (typically a copy stream beside the stream running the layer). The pages
+ * are written where they sit; since the layer reads every weight through the
+ * page table, the expert is usable as soon as its page-table rows name these
+ * pages and the copies have completed on hip_stream.
+ *   pool_base   device, 256-byte aligned; pool_bytes its size.
+ *   pt_rows     host int32 [3][P]: destination page indices (units of
+ *               page_bytes) for w1, w3, w2, as the expert view allocated
+ *               them; every page must lie inside the pool (else ERANGE).
+ *   host_src    host memory, [3][proj_bytes] contiguous, 16-byte aligned;
+ *               page-locked (hipHostMalloc, or pinned by its allocator) so
+ *               the copies run asynchronously. The caller keeps it alive and
+ *               unmodified until the copies complete.
+ *   proj_bytes  bytes of one projection, <= P*page_bytes, a multiple of 16;
+ *               page_bytes a multiple of 128.
+ * Errors: EINVAL, ERANGE (checked before anything is enqueued), EHIP (a copy
+ * could not be enqueued; earlier pages of this call may have been). */
+rimuru_status rimuru_expert_upload(void* pool_base, uint64_t pool_bytes, const int32_t* pt_rows,
+                                   int32_t P, uint64_t page_bytes, const void* host_src,
+                                   uint64_t proj_bytes, void* hip_stream);
+
 /* Small event helpers so callers can time stages without linking HIP:
  * create/destroy a timing-enabled hipEvent_t, and the elapsed milliseconds
  * between two recorded events (synchronises on the second). */

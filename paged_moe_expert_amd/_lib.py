@@ -67,6 +67,8 @@ _PROTOS = {
     "rimuru_pt_check": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_uint64, C.c_uint64]),
     "rimuru_experts_store": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_uint64,
                                          C.c_void_p, C.c_uint64, C.c_void_p]),
+    "rimuru_expert_upload": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_int32, C.c_uint64,
+                                         C.c_void_p, C.c_uint64, C.c_void_p]),
     "rimuru_event_create": (C.c_int32, [C.POINTER(C.c_void_p)]),
     "rimuru_event_destroy": (C.c_int32, [C.c_void_p]),
     "rimuru_event_record": (C.c_int32, [C.c_void_p, C.c_void_p]),

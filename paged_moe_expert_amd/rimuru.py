@@ -200,6 +200,29 @@ def experts_store(pool, pt, weights, page_bytes: int, stream=None) -> None:
                                      weights.data_ptr(), proj_bytes, s.cuda_stream), "experts_store")
 
 
+def expert_upload_raw(pool_ptr: int, pool_bytes: int, pt_rows, page_bytes: int, host_ptr: int,
+                      proj_bytes: int, stream_handle: int) -> int:
+    """Status of rimuru_expert_upload for raw pointers (validation tests)."""
+    rows = np.ascontiguousarray(pt_rows, dtype=np.int32)
+    return lib().rimuru_expert_upload(pool_ptr, pool_bytes, rows.ctypes.data_as(C.c_void_p), rows.shape[-1],
+                                      page_bytes, host_ptr, proj_bytes, stream_handle)
+
+
+def expert_upload(pool, pt_rows, page_bytes: int, host, stream=None) -> None:
+    """Copy one expert's projections host [3, proj_bytes] (pinned CPU tensor)
+    into the pool pages pt_rows [3, P] (host int32) names, asynchronously on
+    stream (default: the current stream)."""
+    import torch
+    if host.device.type != "cpu" or not host.is_pinned():
+        raise ValueError("expert_upload: host weights must be a pinned CPU tensor")
+    if not host.is_contiguous():
+        raise ValueError("expert_upload: host weights must be contiguous")
+    proj_bytes = host[0].numel() * host.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(pool.device)
+    check(expert_upload_raw(pool.data_ptr(), pool.numel() * pool.element_size(), pt_rows, page_bytes,
+                            host.data_ptr(), proj_bytes, s.cuda_stream), "expert_upload")
+
+
 # ----------------------------------------------------------------- timing helpers
 
 def event_create() -> int:

@@ -117,3 +117,29 @@ def test_product_never_imports_the_oracle():
         if f.endswith(".py"):
             txt = open(os.path.join(ROOT, "oracle", f)).read()
             assert "paged_moe_expert_amd" not in txt and "rimuru" not in txt.replace("Rimuru", ""), f
+
+
+def test_expert_upload_validates_before_copying():
+    rows = np.arange(3 * 4, dtype=np.int32).reshape(3, 4)
+    pool, host = 1 << 20, 1 << 21                        # never dereferenced: validation fails first
+    ok_args = dict(pool_ptr=pool, pool_bytes=64 * 4096, page_bytes=4096, host_ptr=host, proj_bytes=4 * 4096,
+                   stream_handle=0)
+
+    def status(pt_rows=rows, **over):
+        a = dict(ok_args, **over)
+        return R.expert_upload_raw(a["pool_ptr"], a["pool_bytes"], pt_rows, a["page_bytes"], a["host_ptr"],
+                                   a["proj_bytes"], a["stream_handle"])
+
+    assert status(pool_ptr=0) == _lib.EINVAL
+    assert status(host_ptr=0) == _lib.EINVAL
+    assert status(pool_ptr=pool + 16) == _lib.EINVAL    # pool_base not 256-byte aligned
+    assert status(host_ptr=host + 8) == _lib.EINVAL     # host_src not 16-byte aligned
+    assert status(page_bytes=100) == _lib.EINVAL
+    assert status(proj_bytes=5 * 4096) == _lib.EINVAL   # more than P pages
+    assert status(proj_bytes=4096 + 8) == _lib.EINVAL   # not a multiple of 16
+    bad = rows.copy()
+    bad[2, 3] = 64                                       # one page past the pool's end
+    assert status(pt_rows=bad) == _lib.ERANGE
+    assert "projection 2, page 3" in _lib.lib().rimuru_last_error().decode()
+    bad[2, 3] = -1
+    assert status(pt_rows=bad) == _lib.ERANGE
