@@ -262,16 +262,21 @@ __device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
 constexpr int kMtBM = 128;     // tile rows
 constexpr int kMtSN = 256;     // columns of one weight sub-tile (512-byte rows)
 #ifndef RIMURU_MT_GM
-#define RIMURU_MT_GM 32
+#define RIMURU_MT_GM 1
 #endif
-constexpr int kMtGM = RIMURU_MT_GM;   // row tiles walked per column tile
+// row tiles walked per column tile; 1 = the column tiles of one row tile run
+// back to back, sharing its A rows in L2 (measured 2% faster than 8 or 32 on
+// the fragmented-prefill layer)
+constexpr int kMtGM = RIMURU_MT_GM;
 
-// One workgroup of 4 wavefronts (one per SIMD) computes a 128-row tile
-// against two 256-column weight sub-tiles: w1 and w3 at the same columns when
-// GATED, else two adjacent column ranges of w2. Wavefront w owns columns
-// 64w .. 64w+63 of each sub-tile for all 128 rows: 4 x 2 x 2 tiles of 32x32
-// (256 accumulators, held in AGPRs), 16 MFMAs per 16-deep K step against 4
-// A and 4 B operand reads.
+// One workgroup of NW wavefronts computes a 128-row tile against two
+// 256-column weight sub-tiles: w1 and w3 at the same columns when GATED, else
+// two adjacent column ranges of w2. Wavefront (wm, wn) owns columns
+// 64wn .. 64wn+63 of each sub-tile for 128/(NW/4) rows: with NW = 4 (one per
+// SIMD) 4 x 2 x 2 tiles of 32x32 (256 accumulators), with NW = 8 (two per
+// SIMD, the default: one wavefront's MFMAs cover the other's copy and LDS
+// read issue) 2 x 2 x 2 tiles (128 accumulators, 8 MFMAs per 16-deep K step
+// against 2 A and 4 B operand reads).
 //
 // Operands reach LDS by asynchronous global->LDS copies (16 bytes per lane;
 // each wavefront instruction fills 1 KB of LDS), STAGES stages of BK rows
@@ -287,13 +292,13 @@ constexpr int kMtGM = RIMURU_MT_GM;   // row tiles walked per column tile
 // reading with the stage STAGES ahead, and reads the next stage's first
 // operands between the last MFMAs of the current stage.
 //
-// Measured on the fragmented-prefill layer (8192 tokens, 128 experts): the
-// wait for copies stays near 100 cycles a stage and the MFMAs alone take
-// ~1180 cycles of the ~2400 a stage costs; the rest is instruction issue
-// (copy, address and LDS-read instructions between MFMAs) at one wavefront
-// per SIMD.
-template <bool GATED, int BK, int STAGES>
-__global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
+// Measured on the fragmented-prefill layer (8192 tokens, 128 experts), with
+// NW = 4: the wait for copies stays near 100 cycles a stage and the MFMAs
+// alone take ~1180 cycles of the ~2400 a stage costs; the rest is instruction
+// issue (copy, address and LDS-read instructions between MFMAs) at one
+// wavefront per SIMD. NW = 8 brings a stage to ~2000-2100 cycles.
+template <bool GATED, int BK, int STAGES, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_paged_gemm_mt(GemmArgs a) {
   constexpr int KS = BK / 16;                     // MFMA K steps per stage
   constexpr int A_CHUNKS = (kMtBM / 32) * KS;     // 1 KB chunks (row block, K step)
   constexpr int A_BYTES = A_CHUNKS * 1024;
@@ -302,13 +307,19 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   constexpr int CHUNK_PITCH = 1024 + 64;          // LDS bytes per chunk (padded)
   constexpr int SUB_LDS = SUB_CHUNKS * CHUNK_PITCH;
   constexpr int STAGE_BYTES = A_BYTES + 2 * SUB_LDS;
-  constexpr int A_DMA = A_CHUNKS / 4;             // per wavefront per stage
-  constexpr int B_DMA = 2 * SUB_BYTES / 1024 / 4;
+  constexpr int NT = NW * 64;
+  constexpr int A_DMA = A_CHUNKS / NW;            // per wavefront per stage
+  constexpr int B_DMA = 2 * SUB_CHUNKS / NW;
   constexpr int DMA = A_DMA + B_DMA;
   constexpr int NBM = GATED ? 2 : 1;              // weight matrices read
-  static_assert(KS >= 2 && KS % 2 == 0 && A_CHUNKS % 4 == 0 && A_DMA == KS && BK % 8 == 0, "stage shape");
+  // wavefront grid: WGM row groups x 4 column groups; TM row blocks of 32 each
+  constexpr int WGM = NW / 4;
+  constexpr int TM = 4 / WGM;
+  constexpr int NMMA = TM * 4;                    // MFMAs per K step
+  constexpr int NREAD = TM + 8;                   // operand reads per K step
+  static_assert((NW == 4 || NW == 8) && A_CHUNKS % NW == 0 && (2 * SUB_CHUNKS) % NW == 0, "wavefronts");
+  static_assert(KS == 2 && BK % 8 == 0, "the K-step schedule below is laid out for two K steps a stage");
   static_assert(STAGES >= 2 && (STAGES - 1) * DMA < 64, "copies in flight");
-  static_assert(KS == 2 && DMA <= 12, "the K-step schedule below is laid out for two K steps a stage");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
   __shared__ int32_t row_slot[kMtBM];
@@ -337,6 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;              // row group, column group
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)));
@@ -344,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   const int nk = a.K / BK;
 
   // ---- page addresses and the tile's row -> slot map
-  for (int i = tid; i < NBM * a.P; i += 256) {
+  for (int i = tid; i < NBM * a.P; i += NT) {
     const int b = i / a.P, q = i - b * a.P;
     const int32_t pg = a.pt[static_cast<int64_t>(e * 3 + (GATED ? b : 2)) * a.P + q];
     page_base[i] = reinterpret_cast<uint64_t>(a.pool) + static_cast<uint64_t>(static_cast<uint32_t>(pg)) * page;
@@ -449,11 +461,11 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   for (int jj = 0; jj < 2; ++jj) {
     // rows 8*(grp/2) + sl/4 (+4 for the upper half): chunk 4*(grp/2) + sl/4
     const int chunk = 4 * (grp >> 1) + (sl >> 2);
-    const int col = 64 * w + 32 * jj + 16 * (grp & 1) + 4 * (sl & 3);
+    const int col = 64 * wn + 32 * jj + 16 * (grp & 1) + 4 * (sl & 3);
     boff[jj] = A_BYTES + chunk * CHUNK_PITCH + col * 2;
   }
   typedef __attribute__((address_space(3))) v4i16 lds_v4;
-  struct Frags { u32x4 a[4]; u32x4 b[2][2]; };
+  struct Frags { u32x4 a[TM]; u32x4 b[2][2]; };
   // A operand of K step s, row block i: lane l reads row 32i + l%32, octet
   // 2s + l/32 (slot swizzled as stored)
   uint32_t aoff[KS];
@@ -463,14 +475,14 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
     const int oct = 2 * s2 + (lane >> 5);
     aoff[s2] = row * (2 * BK) + ((oct ^ ((row >> 2) & (OPR - 1))) * 16);
   }
-  // operand read k (0..11) of K step s: A row blocks 0..3, then the lower
-  // and upper halves of the 4 B operands
+  // operand read k (0..NREAD-1) of K step s: the wavefront's A row blocks,
+  // then the lower and upper halves of the 4 B operands
   auto read_one = [&](Frags& f, int st, int s, int k) {
     const uint8_t* base = smem + (st % STAGES) * STAGE_BYTES;
-    if (k < 4) {
-      f.a[k] = *reinterpret_cast<const u32x4*>(base + k * 32 * (2 * BK) + aoff[s]);
+    if (k < TM) {
+      f.a[k] = *reinterpret_cast<const u32x4*>(base + (wm * TM + k) * 32 * (2 * BK) + aoff[s]);
     } else {
-      const int b = (k - 4) >> 2, jj = ((k - 4) >> 1) & 1, half = (k - 4) & 1;
+      const int b = (k - TM) >> 2, jj = ((k - TM) >> 1) & 1, half = (k - TM) & 1;
       // K step s: rows +16s = chunks +8s; the upper 4 rows: second half of each chunk
       const uint8_t* p = base + boff[jj] + b * SUB_LDS + s * 8 * CHUNK_PITCH + half * 512;
       const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)p));
@@ -480,19 +492,19 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   };
   auto read_frags = [&](Frags& f, int st, int s) {
 #pragma unroll
-    for (int k = 0; k < 12; ++k) read_one(f, st, s, k);
+    for (int k = 0; k < NREAD; ++k) read_one(f, st, s, k);
   };
 
-  f32x16 acc[4][2][2];
+  f32x16 acc[TM][2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][b][jj][r] = 0.0f;
-  // MFMA t (0..15) of one K step: row block t/4, sub-tile (t/2)%2, column block t%2
+  // MFMA t (0..NMMA-1) of one K step: row block t/4, sub-tile (t/2)%2, column block t%2
   auto mma = [&](const Frags& f, int t) {
     const int i = t >> 2, b = (t >> 1) & 1, jj = t & 1;
     acc[i][b][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
@@ -516,28 +528,33 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   Frags fr[2];
   read_frags(fr[0], 0, 0);
 
-  // One wavefront per SIMD issues everything in order, so every operand
-  // read, address step and copy sits in its own slot between two MFMAs (the
-  // matrix pipe runs the earlier MFMA meanwhile); scheduling barriers keep
-  // that order.
-  //   K step 0: MFMA t, then operand read t of K step 1 (t < 12), the
-  //             refill's page-address reads (4 <= t < 12) and their
-  //             advance (t >= 12).
-  //   K step 1: two MFMAs, the wait for stage st+1 and the barrier, then
-  //             MFMA t with operand read t-2 of the next stage and copy t-2
-  //             of the refill.
+  // Each wavefront issues everything in order, so every operand read,
+  // address step and copy sits in a slot between two MFMAs (the matrix pipe
+  // runs the earlier MFMA meanwhile); scheduling barriers keep that order.
+  //   K step 0: the MFMAs, with the operand reads of K step 1, the refill's
+  //             page-address reads (first half) and their advance (second
+  //             half) spread between them.
+  //   K step 1: two MFMAs, the wait for stage st+1 and the barrier, then the
+  //             remaining MFMAs with the next stage's operand reads and the
+  //             refill copies spread between them.
   for (int st = 0; st < nk; ++st) {
     const bool refill = st + STAGES < nk;
     const bool more = st + 1 < nk;
     if (refill) sr.st = next_st;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < NMMA; ++t) {
       mma(fr[0], t);
-      if (t < 12) read_one(fr[1], st, 1, t);
-      if (refill && t >= 4 && t < 12) lookup_one(sr, t - 4);
-      if (refill && t >= 12) {
-        advance_one(2 * (t - 12));
-        advance_one(2 * (t - 12) + 1);
+#pragma unroll
+      for (int k = t * NREAD / NMMA; k < (t + 1) * NREAD / NMMA; ++k) read_one(fr[1], st, 1, k);
+      if (refill) {
+        constexpr int H = NMMA / 2;
+        if (t < H) {
+#pragma unroll
+          for (int d = t * B_DMA / H; d < (t + 1) * B_DMA / H; ++d) lookup_one(sr, d);
+        } else {
+#pragma unroll
+          for (int d = (t - H) * B_DMA / H; d < (t - H + 1) * B_DMA / H; ++d) advance_one(d);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -553,10 +570,17 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 2; t < 16; ++t) {
+    for (int t = 2; t < NMMA; ++t) {
       mma(fr[1], t);
-      if (more && t - 2 < 12) read_one(fr[0], st + 1, 0, t - 2);
-      if (refill && t - 2 < DMA) copy(sr, st + STAGES, t - 2);
+      constexpr int R = NMMA - 2;
+      if (more) {
+#pragma unroll
+        for (int k = (t - 2) * NREAD / R; k < (t - 1) * NREAD / R; ++k) read_one(fr[0], st + 1, 0, k);
+      }
+      if (refill) {
+#pragma unroll
+        for (int d = (t - 2) * DMA / R; d < (t - 1) * DMA / R; ++d) copy(sr, st + STAGES, d);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -574,15 +598,15 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   auto stash = [&](int i, int r, int col_in_sub, float v0, float v1) {
     const float y = swap_lane_pair(odd ? v0 : v1);
     const float lo = odd ? y : v0, hi = odd ? v1 : y;
-    const int trow = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
+    const int trow = 32 * (wm * TM + i) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
     const int col = col_in_sub - (odd ? 1 : 0);
     tile[trow * PAIRS + (col >> 1)] = pack_bf16x2(lo, hi);
   };
-  // 16-byte pieces of the tile: 32 per row, 4096 in all, 16 per thread
+  // 16-byte pieces of the tile: 32 per row, 4096 in all
   auto drain = [&](auto&& row_dst) {
 #pragma unroll 4
-    for (int p = 0; p < kMtBM * kMtSN / 8 / 256; ++p) {
-      const int idx = p * 256 + tid;
+    for (int p = 0; p < kMtBM * kMtSN / 8 / NT; ++p) {
+      const int idx = p * NT + tid;
       const int trow = idx >> 5, piece = idx & 31;
       uint16_t* dst = row_dst(trow);
       if (dst != nullptr)
@@ -596,12 +620,12 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
   __syncthreads();                                          // operand buffers are free
   if constexpr (GATED) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
-          stash(i, r, 64 * w + 32 * jj + (lane & 31),
+          stash(i, r, 64 * wn + 32 * jj + (lane & 31),
                 silu_fast(acc[i][0][jj][r]) * acc[i][1][jj][r],
                 silu_fast(acc[i][0][jj][r + 1]) * acc[i][1][jj][r + 1]);
     __syncthreads();
@@ -611,10 +635,10 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
     for (int b = 0; b < 2; ++b) {
       if (b) __syncthreads();                               // first half drained
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const int trow = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
+          const int trow = 32 * (wm * TM + i) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
           const float wt = row_w[trow];
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
@@ -622,7 +646,7 @@ __global__ __launch_bounds__(256, 1) void k_paged_gemm_mt(GemmArgs a) {
             const float v0 = acc[i][b][jj][r], v1 = acc[i][b][jj][r + 1];
             const float y = swap_lane_pair(odd ? v0 : v1);
             const float lo = wt * (odd ? y : v0), hi = wt * (odd ? v1 : y);
-            const int col = 64 * w + 32 * jj + (lane & 31) - (odd ? 1 : 0);
+            const int col = 64 * wn + 32 * jj + (lane & 31) - (odd ? 1 : 0);
             tile[trow * PAIRS + (col >> 1)] = pack_bf16x2(lo, hi);
           }
         }
@@ -680,12 +704,12 @@ hipError_t launch_gemm(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
 // K rows per stage and stages of the asynchronous pipeline (compile-time
 // overridable for tuning sweeps)
 #ifndef RIMURU_MT
-#define RIMURU_MT 32, 3
+#define RIMURU_MT 32, 3, 8
 #endif
 #ifndef RIMURU_MT_ENABLE
 #define RIMURU_MT_ENABLE 1
 #endif
-struct MtShape { int bk, stages; };
+struct MtShape { int bk, stages, waves; };
 constexpr int kMtPtMax = 2048;    // page addresses the pipelined kernel stages in LDS (16 KB)
 constexpr MtShape kMt{RIMURU_MT};
 
@@ -701,7 +725,8 @@ hipError_t launch_mt(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   const uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / bnw);
   const uint64_t grid = (blocks + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_paged_gemm_mt<GATED, kMt.bk, kMt.stages>), dim3(static_cast<uint32_t>(grid)), dim3(256),
+  hipLaunchKernelGGL((k_paged_gemm_mt<GATED, kMt.bk, kMt.stages, kMt.waves>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(kMt.waves * 64),
                      static_cast<size_t>(nbm) * g.P * sizeof(uint64_t), st, g);
   return hipGetLastError();
 }
