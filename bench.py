@@ -149,6 +149,8 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--upload-experts", type=int, default=8,
                     help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
+    ap.add_argument("--no-router", action="store_true",
+                    help="skip the run that computes the router projection in the gating stage")
     ap.add_argument("--no-contiguous", action="store_true",
                     help="skip the comparison run on a contiguous layout of the same weights")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -281,6 +283,30 @@ def main():
         del cpool
         cont = {"ms_per_step": round(cont_ms, 4), "bitwise_equal_output": same}
 
+    # Timed region 5: the same layer computing its router logits x . w_gate^T
+    # in the gating stage (w_gate [E, H] instead of given logits).
+    router = None
+    if not args.no_router:
+        wg = torch.from_numpy(gen.gate_weight_bits(cfg).view(idt)).to(dev).view(tdt)
+
+        def rstep(events=None):
+            R.fused_moe_paged(x, None, pool, ptd, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs, w_gate=wg,
+                              stage_events=events)
+        for _ in range(args.warmup):
+            rstep()
+        r_secs, _ = timed(rstep)
+        rev = [R.event_create() for _ in range(R.MOE_STAGES + 1)]
+        gate_ms = []
+        for _ in range(5):
+            rstep(rev)
+            torch.cuda.synchronize()
+            gate_ms.append(R.event_elapsed_ms(rev[0], rev[1]))
+        for e_ in rev:
+            R.event_destroy(e_)
+        router = {"ms_per_step": round(r_secs * 1e3 / args.steps, 4),
+                  "gating_with_router_us_median": round(float(np.median(gate_ms)) * 1e3, 2),
+                  "router_gflop": round(2.0 * T * cfg.E * cfg.H / 1e9, 4)}
+
     # Timed region 4: dual-buffer expert upload (host -> fresh expert pages on a
     # copy stream), alone and overlapped with the layer on the compute stream.
     upload = None
@@ -364,6 +390,9 @@ def main():
     }
     if upload is not None:
         out["expert_upload"] = upload
+    if router is not None:
+        router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
+        out["with_router"] = router
     if cont is not None:
         cont["paged_over_contiguous_minus_1"] = round(ms_step / cont["ms_per_step"] - 1.0, 4)
         out["contiguous"] = cont

@@ -233,6 +233,20 @@ rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32_t H, int32
  * Errors: EINVAL, EDTYPE, EHIP (a launch or event record failed). */
 rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream);
 
+/* The same layer with the router projection inside the gating stage (the
+ * upstream step the pages leave implicit): logits[t, e] = x[t] . w_gate[e],
+ * accumulated in fp32 with MFMA tiles by one small GEMM kernel, then the same
+ * top-k and softmax. The logits go to logits_out, or to the workspace (its
+ * size from rimuru_moe_sizes covers them) when logits_out is NULL.
+ *   w_gate      device [E, H] row-major (a Linear layer's weight layout), in
+ *               the layer's dtype, 16-byte aligned.
+ *   logits_out  device [T, E] fp32, or NULL.
+ *   a->logits   not read (may be NULL); every other field as above.
+ * Ties in the top-k are decided on these fp32 logits.
+ * Errors: EINVAL, EDTYPE, EHIP. */
+rimuru_status rimuru_fused_moe_paged_router(const rimuru_moe_args* a, const void* w_gate,
+                                            float* logits_out, void* hip_stream);
+
 /* Host-side check that every entry of a host copy of pt (E*3*P entries)
  * names a page inside a pool of pool_bytes bytes. ERANGE names the first bad
  * entry. */

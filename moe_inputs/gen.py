@@ -21,7 +21,7 @@ import numpy as np
 from .configs import CONV_REQ_MAX, KV_REQ_MAX, MoEConfig
 
 # Stream ids.
-S_X, S_LOGITS, S_WEIGHTS, S_EVENTS, S_UNIFORMS, S_ADJUST, S_POISON = range(7)
+S_X, S_LOGITS, S_WEIGHTS, S_EVENTS, S_UNIFORMS, S_ADJUST, S_POISON, S_GATE = range(8)
 
 # Owner-id ranges for filler requests (expert owners are small integers).
 OWNER_KV = 1 << 32
@@ -84,6 +84,13 @@ def logits(cfg: MoEConfig, T: int | None = None, seed_key: int = 0) -> np.ndarra
     else:
         raise ValueError(cfg.logits)
     return np.ascontiguousarray(out)
+
+
+def gate_weight_bits(cfg: MoEConfig) -> np.ndarray:
+    """Router weights w_gate [E, H] (a Linear layer's layout) as storage bits,
+    N(0, 0.02) like the expert weights."""
+    g = rng(cfg.cid, S_GATE)
+    return encode(g.normal(0.0, 0.02, size=(cfg.E, cfg.H)).astype(np.float32), cfg.dtype)
 
 
 def expert_weight_bits(cfg: MoEConfig, e: int) -> np.ndarray:

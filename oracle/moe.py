@@ -16,6 +16,9 @@ What is computed, and where it comes from:
   reading. Ties in the logits go to the lower expert index, -0 equals +0.
 * Combine: y[t] = sum over j of w[t, j] * expert_{ids[t, j]}(x[t]), j in
   rank order.
+* Router projection (the step upstream of routing that the pages leave
+  implicit): logits[t, e] = x[t] . w_gate[e], w_gate [E, H] in a Linear
+  layer's layout. ``router_logits`` computes it in fp64.
 
 Parity status: pinned. Routing by brute-force sorting, closed forms and the
 k = E special case; page resolution by layout-permutation invariance and a
@@ -43,6 +46,14 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- routing
+
+def router_logits(x_bits: np.ndarray, w_gate_bits: np.ndarray, dtype: str) -> np.ndarray:
+    """logits [T, E] = x [T, H] @ w_gate [E, H]^T in fp64 (inputs decoded
+    exactly from their storage bits)."""
+    x = decode(np.asarray(x_bits).reshape(-1), dtype).reshape(np.asarray(x_bits).shape)
+    wg = decode(np.asarray(w_gate_bits).reshape(-1), dtype).reshape(np.asarray(w_gate_bits).shape)
+    return x @ wg.T
+
 
 def route(logits: np.ndarray, k: int):
     """Top-k experts per token and their renormalised softmax weights.

@@ -217,12 +217,24 @@ struct GemmArgs {
 
 PageDiv make_div(uint32_t page);
 
+// The router projection run in the gating stage instead of taking given
+// logits: x [T, H] and w_gate [E, H] in the layer's dtype; the logits [T, E]
+// fp32 go to logits_out (caller memory, or the layer's workspace).
+struct RouterArgs {
+  const void* x;
+  const void* w_gate;
+  int H;
+  bool bf16;
+  float* logits_out;
+};
+
 // Routing (gating top-k, per-expert sort padded to bm-row tiles) on stream st;
-// counts/tile_expert live in the workspace. stage marks 1 and 2 are recorded
-// between the kernels when ev is not null.
-hipError_t launch_routing(const float* logits, int T, int E, int k, int bm, int32_t* topk_ids,
-                          float* topk_w, int32_t* counts, int32_t* sorted_ids, int32_t* expert_off,
-                          int32_t* tile_expert, hipEvent_t* ev, hipStream_t st);
+// counts/tile_expert live in the workspace. router == null: top-k of the given
+// logits; else the logits are computed from x and w_gate first. Stage marks 1
+// and 2 are recorded between the kernels when ev is not null.
+hipError_t launch_routing(const float* logits, const RouterArgs* router, int T, int E, int k, int bm,
+                          int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* sorted_ids,
+                          int32_t* expert_off, int32_t* tile_expert, hipEvent_t* ev, hipStream_t st);
 
 // y[t] = sum_j y_slot[t*k+j] (fixed j order)
 template <typename T>

@@ -34,7 +34,7 @@ Plan choose_plan(int64_t T, int E, int k, int64_t P) {
 
 struct Layout {
   uint64_t tiles_max, sorted_len;
-  uint64_t off_counts, off_tiles, off_h, off_yslot, total;
+  uint64_t off_counts, off_tiles, off_logits, off_h, off_yslot, total;
 };
 
 Layout layout_for(int64_t T, int E, int k, int H, int I, int es, int bm) {
@@ -44,7 +44,8 @@ Layout layout_for(int64_t T, int E, int k, int H, int I, int es, int bm) {
   l.sorted_len = l.tiles_max * bm;
   l.off_counts = 0;
   l.off_tiles = align_up(static_cast<uint64_t>(E) * 4);
-  l.off_h = l.off_tiles + align_up(l.tiles_max * 4);
+  l.off_logits = l.off_tiles + align_up(l.tiles_max * 4);        // router logits [T, E] fp32
+  l.off_h = l.off_logits + align_up(static_cast<uint64_t>(T) * E * 4);
   l.off_yslot = l.off_h + align_up(l.sorted_len * static_cast<uint64_t>(I) * es);
   l.total = l.off_yslot + align_up(static_cast<uint64_t>(tk) * H * es);
   return l;
@@ -64,7 +65,8 @@ rimuru_status check_shapes(int64_t T, int E, int k, int H, int I, int dtype) {
 }
 
 template <typename T>
-hipError_t launch_layer(const rimuru_moe_args* a, Plan p, const Layout& lay, hipStream_t st) {
+hipError_t launch_layer(const rimuru_moe_args* a, const RouterArgs* router, Plan p, const Layout& lay,
+                        hipStream_t st) {
   const int T_ = a->T, E = a->E, k = a->k, H = a->H, I = a->I;
   const int TK = T_ * k;
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
@@ -83,7 +85,7 @@ hipError_t launch_layer(const rimuru_moe_args* a, Plan p, const Layout& lay, hip
   };
 
   if ((err = mark(0)) != hipSuccess) return err;
-  if ((err = launch_routing(a->logits, T_, E, k, p.bm, a->topk_ids, a->topk_w, counts, a->sorted_ids,
+  if ((err = launch_routing(a->logits, router, T_, E, k, p.bm, a->topk_ids, a->topk_w, counts, a->sorted_ids,
                             a->expert_off, tile_expert, ev, st)) != hipSuccess)
     return err;
 
@@ -146,7 +148,12 @@ extern "C" rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32
   return RIMURU_OK;
 }
 
-extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream) {
+namespace rimuru {
+namespace {
+
+// Host-side validation and launch shared by the two layer entry points;
+// router == null: the logits are an input.
+rimuru_status run_layer(const rimuru_moe_args* a, const RouterArgs* router, void* hip_stream) {
   if (a == nullptr) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged: args is NULL");
   rimuru_status s = check_shapes(a->T, a->E, a->k, a->H, a->I, a->dtype);
   if (s != RIMURU_OK) return s;
@@ -163,7 +170,7 @@ extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* 
                        a->P, (unsigned long long)a->page_bytes, (unsigned long long)proj);
   if (static_cast<uint64_t>(a->P) * a->page_bytes >= (1ull << 31))
     return rimuru_fail(RIMURU_EINVAL, "a projection's pages must span less than 2 GiB");
-  if (!a->x || !a->logits || !a->pool_base || !a->pt || !a->y || !a->topk_ids || !a->topk_w ||
+  if (!a->x || (!router && !a->logits) || !a->pool_base || !a->pt || !a->y || !a->topk_ids || !a->topk_w ||
       !a->sorted_ids || !a->expert_off || !a->workspace)
     return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged: a required pointer is NULL");
   if (!aligned(a->pool_base, 256) || !aligned(a->workspace, 256) || !aligned(a->x, 16) ||
@@ -178,10 +185,33 @@ extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* 
       (a->stage_events && a->n_stage_events != RIMURU_MOE_STAGES + 1))
     return rimuru_fail(RIMURU_EINVAL, "stage_events needs exactly %d events", RIMURU_MOE_STAGES + 1);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  hipError_t err = (a->dtype == RIMURU_BF16) ? launch_layer<uint16_t>(a, p, lay, st)
-                                             : launch_layer<float>(a, p, lay, st);
+  RouterArgs r2;
+  if (router != nullptr) {
+    r2 = *router;
+    if (r2.logits_out == nullptr)
+      r2.logits_out = reinterpret_cast<float*>(static_cast<uint8_t*>(a->workspace) + lay.off_logits);
+    router = &r2;
+  }
+  hipError_t err = (a->dtype == RIMURU_BF16) ? launch_layer<uint16_t>(a, router, p, lay, st)
+                                             : launch_layer<float>(a, router, p, lay, st);
   if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "launch failed: %s", hipGetErrorString(err));
   return RIMURU_OK;
+}
+
+}  // namespace
+}  // namespace rimuru
+
+extern "C" rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream) {
+  return run_layer(a, nullptr, hip_stream);
+}
+
+extern "C" rimuru_status rimuru_fused_moe_paged_router(const rimuru_moe_args* a, const void* w_gate,
+                                                       float* logits_out, void* hip_stream) {
+  if (a == nullptr) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_router: args is NULL");
+  if (w_gate == nullptr || !aligned(w_gate, 16))
+    return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_router: w_gate must be a 16-byte aligned device pointer");
+  RouterArgs r{a->x, w_gate, a->H, a->dtype == RIMURU_BF16, logits_out};
+  return run_layer(a, &r, hip_stream);   // logits_out == NULL: run_layer points it at the workspace
 }
 
 extern "C" rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int32_t P,

@@ -30,15 +30,32 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   return __uint_as_float(u);
 }
 
+// One max step with a DPP-permuted copy of v (lanes whose row is masked off
+// keep their own value, which the max leaves unchanged).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(v)), hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+  const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false));
+  const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(phi) << 32) | plo;
+  return o > v ? o : v;
+}
+
+// Max over the wavefront's 64 lanes, returned to every lane. DPP moves stay
+// in the VALU (no LDS round trips): pairs, quads, 8 and 16 lanes by quad
+// permutes and row mirrors, then row 0 -> 1 and 2 -> 3 by the lane-15
+// broadcast and rows 0-1 -> 2-3 by the lane-31 broadcast; lane 63 then holds
+// the maximum.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);       // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);       // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);      // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);      // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);      // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);      // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -116,6 +133,109 @@ __global__ __launch_bounds__(256) void k_gating(const float* __restrict__ logits
     ids[static_cast<int64_t>(t) * k + lane] = static_cast<int32_t>(e);
     w[static_cast<int64_t>(t) * k + lane] = wt;
   }
+}
+
+// Router projection as its own small GEMM: logits[t, e] = x[t] . w_gate[e]
+// (w_gate [E, H] row-major, a Linear layer's weight layout), fp32
+// accumulation with 16x16 MFMA tiles; both operands are K-contiguous rows,
+// loaded straight into registers. A workgroup computes 16 tokens x 16*NT
+// experts with its K range split over 8 wavefronts, summed in fixed
+// wavefront order in LDS. Each wavefront loads LA K steps of both operands
+// before multiplying, so a block costs about one memory round trip per LA
+// steps. Few tokens (decode) take NT = 1 so that w_gate's reads spread over
+// as many CUs as possible (one workgroup per token block streaming all of
+// w_gate was measured about twice as slow); many tokens take wider expert
+// tiles so that x is re-read fewer times.
+constexpr int kRouterGW = 8;   // wavefronts per workgroup (K split)
+#ifndef RIMURU_ROUTER_MINWG
+#define RIMURU_ROUTER_MINWG 1024
+#endif
+
+template <typename T, int NT, int LA>
+__global__ __launch_bounds__(kRouterGW * 64) void k_router_logits(const T* __restrict__ x,
+                                                                  const T* __restrict__ w_gate, int T_, int E,
+                                                                  int H, int nsplit, float* __restrict__ logits) {
+  typedef Elt<T> X;
+  constexpr int VEC = X::VEC, SEG8 = X::SEG8;
+  __shared__ float part[kRouterGW][16][16 * NT];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16 * NT;
+  const int fi = lane & 15, fq = lane >> 4;
+  if (wv < nsplit) {
+    const int kw = H / nsplit;   // multiple of 32 (chosen by the launcher)
+    const int ks = wv;           // K slice of this wavefront
+    const T* xa = x + static_cast<int64_t>(min(t0 + fi, T_ - 1)) * H + ks * kw + fq * 8;
+    const T* wr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      wr[n] = w_gate + static_cast<int64_t>(min(e0 + n * 16 + fi, E - 1)) * H + ks * kw + fq * 8;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < kw; kb += 32 * LA) {
+      // Steps past kw re-read the last step with x zeroed: their products are
+      // exact zeros, which leave the fp32 sums unchanged. No branch here, so
+      // every load of the batch is issued before the first MFMA waits.
+      u32x4 a[LA][SEG8], b[LA][NT][SEG8];
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        const int k0 = min(kb + 32 * j, kw - 32);
+#pragma unroll
+        for (int u = 0; u < SEG8; ++u) a[j][u] = *reinterpret_cast<const u32x4*>(xa + k0 + u * VEC);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int u = 0; u < SEG8; ++u) b[j][n][u] = *reinterpret_cast<const u32x4*>(wr[n] + k0 + u * VEC);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        const uint32_t keep = (kb + 32 * j < kw) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int u = 0; u < SEG8; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) a[j][u][c] &= keep;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = X::mma8(a[j], b[j][n], acc[n]);
+      }
+    }
+    // acc[n][r] holds token 4*(lane/16) + r, expert 16n + lane%16
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[ks][4 * fq + r][n * 16 + fi] = acc[n][r];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 16 * NT; i += kRouterGW * 64) {
+    const int tl = i / (16 * NT), el = i % (16 * NT);
+    float v = part[0][tl][el];
+    for (int sw = 1; sw < nsplit; ++sw) v += part[sw][tl][el];
+    const int t = t0 + tl, e = e0 + el;
+    if (t < T_ && e < E) logits[static_cast<int64_t>(t) * E + e] = v;
+  }
+}
+
+template <typename T, int NT, int LA>
+void launch_router_nt(const RouterArgs& r, int n_tok, int E, int nsplit, hipStream_t st) {
+  const dim3 grid((n_tok + 15) / 16, (E + 16 * NT - 1) / (16 * NT));
+  hipLaunchKernelGGL((k_router_logits<T, NT, LA>), grid, dim3(kRouterGW * 64), 0, st,
+                     static_cast<const T*>(r.x), static_cast<const T*>(r.w_gate), n_tok, E, r.H, nsplit,
+                     r.logits_out);
+}
+
+// Widest expert tile that still gives RIMURU_ROUTER_MINWG workgroups; LA
+// keeps about 16 tile loads in flight per lane.
+template <typename T>
+void launch_router(const RouterArgs& r, int n_tok, int E, hipStream_t st) {
+  int nsplit = 1;
+  for (int n = kRouterGW; n > 1; n /= 2)
+    if (r.H % (32 * n) == 0) { nsplit = n; break; }
+  const int64_t tb = (n_tok + 15) / 16, et = (E + 15) / 16;
+  auto blocks = [&](int nt) { return tb * ((et + nt - 1) / nt); };
+  if (blocks(8) >= RIMURU_ROUTER_MINWG) launch_router_nt<T, 8, 2>(r, n_tok, E, nsplit, st);
+  else if (blocks(4) >= RIMURU_ROUTER_MINWG) launch_router_nt<T, 4, 4>(r, n_tok, E, nsplit, st);
+  else if (blocks(2) >= RIMURU_ROUTER_MINWG) launch_router_nt<T, 2, 8>(r, n_tok, E, nsplit, st);
+  else launch_router_nt<T, 1, 8>(r, n_tok, E, nsplit, st);
 }
 
 // ---------------------------------------------------------------- stage 2: count
@@ -302,13 +422,19 @@ PageDiv make_div(uint32_t page) {
   return PageDiv{m, 32 + l, page};
 }
 
-hipError_t launch_routing(const float* logits, int T, int E, int k, int bm, int32_t* topk_ids,
-                          float* topk_w, int32_t* counts, int32_t* sorted_ids, int32_t* expert_off,
-                          int32_t* tile_expert, hipEvent_t* ev, hipStream_t st) {
+hipError_t launch_routing(const float* logits, const RouterArgs* router, int T, int E, int k, int bm,
+                          int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* sorted_ids,
+                          int32_t* expert_off, int32_t* tile_expert, hipEvent_t* ev, hipStream_t st) {
   hipError_t err;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   const int TK = T * k;
   const int epl = (E + 63) / 64;
+  if (router != nullptr) {   // logits = x . w_gate^T first, into router->logits_out
+    if (router->bf16) launch_router<uint16_t>(*router, T, E, st);
+    else launch_router<float>(*router, T, E, st);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    logits = router->logits_out;
+  }
   const dim3 grid((T + 3) / 4);
   if (epl <= 1) hipLaunchKernelGGL(k_gating<1>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);
   else if (epl <= 2) hipLaunchKernelGGL(k_gating<2>, grid, dim3(256), 0, st, logits, T, E, k, topk_ids, topk_w);

@@ -152,24 +152,30 @@ class MoeBuffers:
 
 
 def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
-                    bufs: MoeBuffers | None = None, stream=None, stage_events=None) -> MoeBuffers:
+                    bufs: MoeBuffers | None = None, stream=None, stage_events=None,
+                    w_gate=None, logits_out=None) -> MoeBuffers:
     """Enqueue the fused MoE layer on the current (or given) torch stream.
 
     x [T, H] bf16/fp32, logits [T, E] fp32, pool uint8 device tensor,
     pt int32 [E, 3, P] device tensor, I the intermediate size. Returns the
     buffers holding y, topk_ids, topk_w, sorted_ids and expert_off. Does not
     synchronise.
+
+    With w_gate [E, H] (x's dtype) the router projection runs inside the
+    gating stage (rimuru_fused_moe_paged_router): logits is then not read and
+    may be None; logits_out [T, E] fp32, if given, receives the logits.
     """
     import torch
     T, H = x.shape
-    E = logits.shape[1]
+    E = w_gate.shape[0] if w_gate is not None else logits.shape[1]
     P = pt.shape[2]
     dt = _dtype_code(x)
     if bufs is None:
         bufs = MoeBuffers(T, E, k, H, I, P, dt, device=x.device)
     a = MoeArgs()
     a.T, a.E, a.k, a.H, a.I, a.P, a.dtype, a.renormalize = T, E, k, H, I, P, dt, 1
-    a.x, a.logits, a.pool_base, a.pt = x.data_ptr(), logits.data_ptr(), pool.data_ptr(), pt.data_ptr()
+    a.x, a.pool_base, a.pt = x.data_ptr(), pool.data_ptr(), pt.data_ptr()
+    a.logits = logits.data_ptr() if logits is not None else None
     a.page_bytes = page_bytes
     a.y, a.topk_ids, a.topk_w = bufs.y.data_ptr(), bufs.topk_ids.data_ptr(), bufs.topk_w.data_ptr()
     a.sorted_ids, a.expert_off = bufs.sorted_ids.data_ptr(), bufs.expert_off.data_ptr()
@@ -180,7 +186,14 @@ def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
         a.stage_events = C.cast(ev_arr, C.c_void_p)
         a.n_stage_events = len(stage_events)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
-    check(lib().rimuru_fused_moe_paged(C.byref(a), s.cuda_stream), "fused_moe_paged")
+    if w_gate is None:
+        check(lib().rimuru_fused_moe_paged(C.byref(a), s.cuda_stream), "fused_moe_paged")
+    else:
+        if w_gate.dtype != x.dtype or tuple(w_gate.shape) != (E, H) or not w_gate.is_contiguous():
+            raise ValueError("fused_moe_paged: w_gate must be a contiguous [E, H] tensor of x's dtype")
+        out = logits_out.data_ptr() if logits_out is not None else None
+        check(lib().rimuru_fused_moe_paged_router(C.byref(a), w_gate.data_ptr(), out, s.cuda_stream),
+              "fused_moe_paged_router")
     return bufs
 
 

@@ -317,3 +317,40 @@ def test_generated_bf16_rounding_is_nearest_even():
     a = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -(1 + 2 ** -7)], dtype=np.float32)
     b = gen.f32_to_bf16_bits(a)
     assert decode(b, "bf16").tolist() == [1.0, 1 + 2 ** -6, 1.0, -(1 + 2 ** -7)]
+
+
+# ---------------------------------------------------------------- router projection
+
+def _bits_f32(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def test_router_logits_brute_force_loops():
+    """logits[t, e] = sum_h x[t, h] * w_gate[e, h], checked with plain loops."""
+    g = np.random.default_rng(7)
+    x = g.standard_normal((3, 5)).astype(np.float32)
+    wg = g.standard_normal((4, 5)).astype(np.float32)
+    from oracle.moe import router_logits
+    got = router_logits(_bits_f32(x), _bits_f32(wg), "f32")
+    for t in range(3):
+        for e in range(4):
+            ref = math.fsum(float(x[t, h]) * float(wg[e, h]) for h in range(5))
+            assert got[t, e] == pytest.approx(ref, rel=1e-15, abs=1e-15)
+
+
+def test_router_logits_hand_values_and_structure():
+    from oracle.moe import router_logits
+    x = np.array([[1.0, 2.0, 0.5]], dtype=np.float32)
+    wg = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 2.0], [-1.0, -1.0, -1.0]], dtype=np.float32)
+    assert router_logits(_bits_f32(x), _bits_f32(wg), "f32").tolist() == [[1.0, 3.0, -3.5]]
+    # permuting the experts (rows of w_gate) permutes the logit columns
+    g = np.random.default_rng(3)
+    xb = gen.encode(g.standard_normal((6, 64)).astype(np.float32), "bf16")
+    wb = gen.encode(g.standard_normal((8, 64)).astype(np.float32), "bf16")
+    perm = g.permutation(8)
+    a = router_logits(xb, wb, "bf16")
+    b = router_logits(xb, wb[perm], "bf16")
+    assert np.array_equal(b, a[:, perm])
+    # bf16 inputs decode exactly: the logits equal the fp64 dot products of the decoded values
+    xd, wd = decode(xb.reshape(-1), "bf16").reshape(6, 64), decode(wb.reshape(-1), "bf16").reshape(8, 64)
+    assert np.array_equal(a, xd @ wd.T)
