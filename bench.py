@@ -78,6 +78,62 @@ def cpu_baseline(cfg, xb, lg, wb, n_tokens: int):
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
+def adjuster_bench(cfg, R, np, gen, upload_gbs):
+    """Host-side cost of the adjuster policy on this layer's pool: a seeded
+    synthetic serving trace (rising and falling request rate, chat-like
+    lengths) drives the native adjuster over the layer's expert and KV views;
+    each step's call is timed (ctypes marshalling included), and the experts it
+    loads are priced at the measured upload rate."""
+    import time as _t
+    xs, ks = cfg.view("expert"), cfg.view("kv")
+    pool = R.pool_create(cfg.pool_bytes, cfg.huge_bytes)
+    xv = R.view_map(pool, xs.kind, xs.page_bytes)
+    kv = R.view_map(pool, ks.kind, ks.page_bytes, xv)
+    for e in range(cfg.E):
+        for p in range(3):
+            R.view_alloc(xv, 3 * e + p, cfg.P)
+    usable = R.pool_stats(pool)["huge_pages"] * cfg.huge_bytes
+    xb = cfg.E * 3 * cfg.P * xs.page_bytes
+    R.view_set_budget(xv, xb)
+    R.view_set_budget(kv, usable - xb)
+    prm = dict(min_resident=96, headroom_blocks=256, return_blocks=2048, shift=3, max_prefetch=4)
+    adj = R.adjuster_create(pool, xv, kv, cfg.E, cfg.P, **prm)
+    blocks, routed, _ = gen.serving_trace(31, 300, cfg.E, cfg.k, mean_arrivals=30.0, prompt_mu=5.5,
+                                          output_mu=4.8, max_step_tokens=8, phase_steps=60, period=100)
+    owners, us, ev, ld, met = [], [], 0, 0, 0
+    kvb = ks.page_bytes
+    for st in range(len(blocks)):
+        d = int(blocks[st])
+        needed = (routed[st] > 0).astype(np.uint8)
+        t0 = _t.perf_counter()
+        r = R.adjuster_step(adj, d, routed[st], needed)
+        us.append((_t.perf_counter() - t0) * 1e6)
+        ev += len(r["evicted"])
+        ld += len(r["loaded"])
+        for e in r["loaded"]:
+            R.adjuster_upload_done(adj, e)
+        budget = R.view_usage(kv)[1]
+        met += budget >= d * kvb
+        target = min(d, budget // kvb)
+        held = sum(n for _, n in owners)
+        while owners and held > target:
+            o, n = owners.pop()
+            R.view_free(kv, o)
+            held -= n
+        if target > held and R.view_alloc_status(kv, (1 << 40) + st, target - held)[0] == R.OK:
+            owners.append(((1 << 40) + st, target - held))
+    n = len(blocks)
+    mb = ld * 3 * cfg.proj_bytes / n / 1e6
+    out = {"trace_steps": n, "host_us_per_step_median": round(float(np.median(us)), 1),
+           "host_us_per_step_p99": round(float(np.percentile(us, 99)), 1),
+           "evictions_per_step": round(ev / n, 2), "loads_per_step": round(ld / n, 2),
+           "upload_mb_per_step": round(mb, 2), "demand_met_fraction": round(met / n, 3),
+           "params": prm}
+    if upload_gbs:
+        out["upload_ms_per_step_at_measured_rate"] = round(mb / 1e3 / upload_gbs * 1e3, 3)
+    return out
+
+
 def expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np):
     """Upload n experts' weights from pinned host memory into fresh pages of
     their own, first alone, then while the layer runs on the compute stream."""
@@ -90,18 +146,26 @@ def expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np):
     side = torch.cuda.Stream(device=dev)
     main = torch.cuda.current_stream(dev)
 
+    # raw entry point with the pointers worked out once: the timed copies are
+    # not held back by per-call argument checks on the host
+    dptr, dbytes, hptr = dst.data_ptr(), dst.numel(), host.data_ptr()
+    rows_c = [np.ascontiguousarray(rows[j]) for j in range(n)]
+    sh = side.cuda_stream
+
     def upload_round():
         for j in range(n):
-            R.expert_upload(dst, rows[j], cfg.page_bytes, host[j], stream=side)
+            R.check(R.expert_upload_raw(dptr, dbytes, rows_c[j], cfg.page_bytes, hptr + j * 3 * proj,
+                                        proj, sh), "expert_upload")
 
     upload_round()                                      # warm
     side.synchronize()
     e0, e1 = R.event_create(), R.event_create()
     R.event_record(e0, side)
-    for _ in range(3):
+    for _ in range(8):
         upload_round()
     R.event_record(e1, side)
-    alone_ms = R.event_elapsed_ms(e0, e1) / 3
+    side.synchronize()
+    alone_ms = R.event_elapsed_ms(e0, e1) / 8
     bytes_round = n * 3 * proj
     # overlapped: enough rounds to cover the timed layer steps
     torch.cuda.synchronize()
@@ -149,6 +213,8 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--upload-experts", type=int, default=8,
                     help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
+    ap.add_argument("--no-adjuster", action="store_true",
+                    help="skip the host-side adjuster policy measurement")
     ap.add_argument("--no-router", action="store_true",
                     help="skip the run that computes the router projection in the gating stage")
     ap.add_argument("--no-contiguous", action="store_true",
@@ -390,6 +456,9 @@ def main():
     }
     if upload is not None:
         out["expert_upload"] = upload
+    if not args.no_adjuster and any(v.name == "kv" and v.parent == "expert" for v in cfg.views):
+        gbs = upload["upload_gbs_alone"] if upload is not None else None
+        out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
     if router is not None:
         router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
         out["with_router"] = router

@@ -149,6 +149,10 @@ rimuru_status rimuru_pool_transfer(rimuru_pool* pool, rimuru_view* from, rimuru_
 /* Bytes held by the view's owners, and its budget (UINT64_MAX = none). */
 rimuru_status rimuru_view_usage(const rimuru_view* v, uint64_t* used_bytes,
                                 uint64_t* budget_bytes);
+/* The pool a view belongs to, its kind and its page size; any output may be
+ * NULL. Errors: EINVAL (NULL view). */
+rimuru_status rimuru_view_info(const rimuru_view* v, rimuru_pool** pool, int32_t* kind,
+                               uint64_t* page_bytes);
 
 typedef struct {
   uint64_t huge_pages;        /* whole huge pages in the pool */
@@ -164,6 +168,90 @@ rimuru_status rimuru_pool_stats(const rimuru_pool* pool, rimuru_pool_stats_t* ou
 /* Full internal consistency check (slow; for tests). EINVAL with a message
  * naming the first broken invariant. */
 rimuru_status rimuru_pool_check(const rimuru_pool* pool);
+
+/* ------------------------------------------------------------------------ */
+/* Workload-aware adjuster policy                                           */
+/* ------------------------------------------------------------------------ */
+
+/* The policy that moves the fence between the expert view and the KV view
+ * (paper summary: abstract, "workload-aware adjuster", and Figure 8;
+ * explainer "Rimuru unifies serving memory", paragraph on the two pieces that
+ * make the moving fence usable: grow the KV side when concurrency climbs,
+ * give space back to the experts when requests finish, and keep expert loads
+ * and evictions from colliding with the prefetch pipeline). The pages give no
+ * rule beyond that; the rule below is this library's reading.
+ *
+ * Experts are expert-view owners 3e + p (p = 0, 1, 2 for w1, w3, w2), P pages
+ * each; expert e is resident when all three hold P pages. Each expert has an
+ * integer popularity score, s <- s - (s >> shift) + (routed << 16) per step.
+ * Pinned experts (needed by the next layer call, or with an upload in
+ * flight) are never evicted. "Coldest" = lowest score, ties to the lower id.
+ * One step, given D = KV blocks demanded:
+ *   1. each needed, non-resident expert (ascending id) gets pages: while the
+ *      expert view's free budget is short of one expert, evict the coldest
+ *      unpinned resident expert; with none left, move the shortfall from the
+ *      KV view's unused budget, else fail (ENOMEM); if the pool itself has
+ *      no room, evict the next coldest and retry;
+ *   2. W = (D + headroom_blocks) KV blocks. Below W: the KV view takes the
+ *      shortfall, capped so that the expert view keeps a budget of
+ *      min_resident experts; coldest unpinned experts are evicted until the
+ *      expert view's free budget covers that amount (or none is left), then
+ *      the free amount moves. Above W by more than return_blocks blocks:
+ *      everything above max(W, KV bytes held) moves back to the experts;
+ *   3. prefetch: while a whole expert of budget is free and fewer than
+ *      max_prefetch prefetches were made, the most popular non-resident
+ *      expert with a positive score not evicted in this step gets pages
+ *      (ties to the lower id); the first that does not fit ends the step.
+ * Loads are reported demand loads first, then prefetches; each loaded
+ * expert is "in flight" until rimuru_adjuster_upload_done: the caller fills
+ * its pages (rimuru_view_pages gives them; rimuru_expert_upload copies from
+ * host memory) and must finish the demand loads before the layer runs.
+ * Page moves never happen: only budgets move and experts come and go. */
+typedef struct rimuru_adjuster rimuru_adjuster; /* opaque, host side */
+typedef struct {
+  int32_t E;               /* experts, >= 1 */
+  int32_t P;               /* expert-view pages per projection, >= 1 */
+  int32_t min_resident;    /* expert budget kept when KV grows, in experts;
+                              must cover the experts one step needs plus the
+                              uploads in flight, or steps can fail */
+  int32_t headroom_blocks; /* KV blocks of slack above the demand */
+  int32_t return_blocks;   /* surplus KV blocks tolerated before giving back */
+  int32_t shift;           /* popularity decay, 0..16 (keeps scores < 2^63) */
+  int32_t max_prefetch;    /* prefetch loads per step, >= 0 */
+} rimuru_adjuster_params;
+
+/* Create the adjuster over two views of one pool; both need finite budgets
+ * (rimuru_view_set_budget). Experts whose three projections already hold P
+ * pages start resident; a partly placed expert is EINVAL. The adjuster does
+ * not own the pool: destroy it before the pool.
+ * Errors: EINVAL. */
+rimuru_status rimuru_adjuster_create(rimuru_pool* pool, rimuru_view* expert_view, rimuru_view* kv_view,
+                                     const rimuru_adjuster_params* params, rimuru_adjuster** out);
+rimuru_status rimuru_adjuster_destroy(rimuru_adjuster* adj); /* NULL is a no-op */
+
+/* One policy step.
+ *   demand_blocks  KV blocks the running and admitted requests need.
+ *   routed         host int32 [E] routed slots per expert in the last step
+ *                  (>= 0), or NULL for none.
+ *   needed         host uint8 [E], nonzero = the next layer call reads the expert.
+ *   evicted, loaded  host int32 arrays of capacity E; *n_evicted/*n_loaded
+ *                  receive the counts (an expert appears at most once in each).
+ *   kv_moved       bytes of budget moved toward the KV view (negative: toward
+ *                  the experts), net over the step; may be NULL.
+ * Errors: EINVAL (bad argument); ENOMEM (the needed experts do not fit):
+ * the evictions and loads made before the failure stand and are reported. */
+rimuru_status rimuru_adjuster_step(rimuru_adjuster* adj, uint64_t demand_blocks, const int32_t* routed,
+                                   const uint8_t* needed, int32_t* evicted, int32_t* n_evicted,
+                                   int32_t* loaded, int32_t* n_loaded, int64_t* kv_moved);
+
+/* The upload into expert e's pages has finished: e is no longer pinned by
+ * it. Errors: EINVAL (no upload of e in flight). */
+rimuru_status rimuru_adjuster_upload_done(rimuru_adjuster* adj, int32_t e);
+
+/* Copy the state out: resident and in_flight as uint8 [E], score as uint64
+ * [E]; any may be NULL. */
+rimuru_status rimuru_adjuster_state(const rimuru_adjuster* adj, uint8_t* resident, uint8_t* in_flight,
+                                    uint64_t* score);
 
 /* ------------------------------------------------------------------------ */
 /* Page-table-aware fused MoE                                               */

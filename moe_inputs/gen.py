@@ -215,3 +215,57 @@ def adjuster_kv_requests(cfg: MoEConfig, B: int, n: int = 20000):
     """KV request sizes (blocks) that grow the KV view during adjuster steps."""
     g = rng(cfg.cid, S_ADJUST, B, 1)
     return [int(v) for v in g.integers(1, KV_REQ_MAX + 1, n)]
+
+
+# ---------------------------------------------------------------- serving trace
+
+S_TRACE = 8
+
+
+def serving_trace(seed: int, steps: int, E: int, k: int, mean_arrivals: float, period: int = 200,
+                  prompt_mu: float = 5.5, output_mu: float = 5.0, sigma: float = 0.9,
+                  zipf_s: float = 1.1, phase_steps: int = 150, block_tokens: int = 16,
+                  max_step_tokens: int | None = None):
+    """A synthetic concurrency trace for the adjuster: per forward step, the
+    KV blocks the running requests hold plus those arriving need, and how
+    many routed slots each expert received.
+
+    Arrivals per step ~ Poisson(mean_arrivals * (1 + 0.8 sin(2 pi s / period)))
+    (a request rate that rises and falls over time); prompt and output lengths
+    ~ lognormal(mu, sigma), clipped to [16, 8192] and [8, 2048] tokens (a
+    chat-like length mix). A running request holds ceil(tokens / block_tokens)
+    KV blocks, gains one token per step and leaves after its output length.
+    Expert popularity is Zipf(s) over a permutation redrawn every phase_steps
+    steps; a step's routed slots (running requests plus the arriving prompts'
+    tokens, at most max_step_tokens of them, k each) are one multinomial draw
+    over that popularity.
+    Returns (blocks int64 [steps], routed int32 [steps, E], concurrency int64 [steps]).
+    """
+    g = rng(seed, S_TRACE, steps, E)
+    running = []                       # [tokens so far, tokens still to generate]
+    blocks = np.zeros(steps, dtype=np.int64)
+    conc = np.zeros(steps, dtype=np.int64)
+    routed = np.zeros((steps, E), dtype=np.int32)
+    ranks = np.arange(1, E + 1, dtype=np.float64) ** -zipf_s
+    p = None
+    for s in range(steps):
+        if s % phase_steps == 0:
+            p = np.empty(E)
+            p[g.permutation(E)] = ranks / ranks.sum()
+        lam = mean_arrivals * (1.0 + 0.8 * np.sin(2.0 * np.pi * s / period))
+        n_new = int(g.poisson(max(lam, 0.0)))
+        prompts = np.clip(np.rint(g.lognormal(prompt_mu, sigma, n_new)), 16, 8192).astype(np.int64)
+        outs = np.clip(np.rint(g.lognormal(output_mu, sigma, n_new)), 8, 2048).astype(np.int64)
+        tokens = len(running) + int(prompts.sum())
+        if max_step_tokens is not None:
+            tokens = min(tokens, max_step_tokens)
+        for r in running:
+            r[0] += 1
+            r[1] -= 1
+        running = [r for r in running if r[1] > 0]
+        running += [[int(a), int(b)] for a, b in zip(prompts, outs)]
+        blocks[s] = sum((r[0] + block_tokens - 1) // block_tokens for r in running)
+        conc[s] = len(running)
+        if tokens:
+            routed[s] = g.multinomial(tokens * k, p)
+    return blocks, routed, conc

@@ -33,6 +33,12 @@ class PoolStats(C.Structure):
                 ("waste_bytes", C.c_uint64), ("split_parents", C.c_uint64)]
 
 
+class AdjusterParams(C.Structure):
+    _fields_ = [("E", C.c_int32), ("P", C.c_int32), ("min_resident", C.c_int32),
+                ("headroom_blocks", C.c_int32), ("return_blocks", C.c_int32), ("shift", C.c_int32),
+                ("max_prefetch", C.c_int32)]
+
+
 class MoeArgs(C.Structure):
     _fields_ = [("T", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("H", C.c_int32),
                 ("I", C.c_int32), ("P", C.c_int32), ("dtype", C.c_int32),
@@ -59,7 +65,17 @@ _PROTOS = {
     "rimuru_view_set_budget": (C.c_int32, [C.c_void_p, C.c_uint64]),
     "rimuru_pool_transfer": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint64]),
     "rimuru_view_usage": (C.c_int32, [C.c_void_p, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
+    "rimuru_view_info": (C.c_int32, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_int32),
+                                     C.POINTER(C.c_uint64)]),
     "rimuru_pool_stats": (C.c_int32, [C.c_void_p, C.POINTER(PoolStats)]),
+    "rimuru_adjuster_create": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(AdjusterParams),
+                                           C.POINTER(C.c_void_p)]),
+    "rimuru_adjuster_destroy": (C.c_int32, [C.c_void_p]),
+    "rimuru_adjuster_step": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.POINTER(C.c_int32), C.c_void_p, C.POINTER(C.c_int32),
+                                         C.POINTER(C.c_int64)]),
+    "rimuru_adjuster_upload_done": (C.c_int32, [C.c_void_p, C.c_int32]),
+    "rimuru_adjuster_state": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "rimuru_pool_check": (C.c_int32, [C.c_void_p]),
     "rimuru_moe_sizes": (C.c_int32, [C.c_int32] * 7 + [C.POINTER(C.c_uint64), C.POINTER(C.c_uint64),
                                                       C.POINTER(C.c_int32)]),

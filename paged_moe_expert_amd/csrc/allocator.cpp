@@ -335,6 +335,15 @@ extern "C" rimuru_status rimuru_view_usage(const rimuru_view* v, uint64_t* used_
   return RIMURU_OK;
 }
 
+extern "C" rimuru_status rimuru_view_info(const rimuru_view* v, rimuru_pool** pool, int32_t* kind,
+                                          uint64_t* page_bytes) {
+  if (v == nullptr) return rimuru_fail(RIMURU_EINVAL, "view_info: NULL view");
+  if (pool) *pool = v->pool;
+  if (kind) *kind = v->kind;
+  if (page_bytes) *page_bytes = v->page;
+  return RIMURU_OK;
+}
+
 extern "C" rimuru_status rimuru_pool_stats(const rimuru_pool* pool, rimuru_pool_stats_t* out) {
   if (pool == nullptr || out == nullptr) return rimuru_fail(RIMURU_EINVAL, "pool_stats: NULL argument");
   rimuru_pool_stats_t s{};

@@ -9,8 +9,8 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, MoeArgs, OK,  # noqa: F401
-                   PoolStats, RimuruError, check, lib)
+from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, AdjusterParams,  # noqa: F401
+                   MoeArgs, OK, PoolStats, RimuruError, check, lib)
 
 
 # ----------------------------------------------------------------- pool and views
@@ -97,6 +97,13 @@ def view_usage(v: View):
     return used.value, (None if budget.value == NO_BUDGET else budget.value)
 
 
+def view_info(v: View):
+    """(kind, page_bytes) as the library records them."""
+    kind, page = C.c_int32(), C.c_uint64()
+    check(lib().rimuru_view_info(v.handle, None, C.byref(kind), C.byref(page)), "view_info")
+    return kind.value, page.value
+
+
 def pool_stats(pool: Pool) -> dict:
     s = PoolStats()
     check(lib().rimuru_pool_stats(pool.handle, C.byref(s)), "pool_stats")
@@ -113,6 +120,69 @@ def pt_check(pt: np.ndarray, page_bytes: int, pool_bytes: int) -> None:
     pt = np.ascontiguousarray(pt, dtype=np.int32)
     E, three, P = pt.shape
     check(lib().rimuru_pt_check(pt.ctypes.data, E, P, page_bytes, pool_bytes), "pt_check")
+
+
+# ----------------------------------------------------------------- adjuster policy
+
+class Adjuster:
+    """Host state of the workload-aware adjuster (keeps its pool alive)."""
+
+    def __init__(self, handle: int, pool: Pool, E: int):
+        self.handle = handle
+        self.pool = pool
+        self.E = E
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib().rimuru_adjuster_destroy(self.handle)
+            self.handle = None
+
+
+def adjuster_create(pool: Pool, expert_view: View, kv_view: View, E: int, P: int, min_resident: int = 0,
+                    headroom_blocks: int = 0, return_blocks: int = 0, shift: int = 3,
+                    max_prefetch: int = 1) -> Adjuster:
+    prm = AdjusterParams(E, P, min_resident, headroom_blocks, return_blocks, shift, max_prefetch)
+    h = C.c_void_p()
+    check(lib().rimuru_adjuster_create(pool.handle, expert_view.handle, kv_view.handle, C.byref(prm),
+                                       C.byref(h)), "adjuster_create")
+    return Adjuster(h.value, pool, E)
+
+
+def adjuster_step_status(adj: Adjuster, demand_blocks: int, routed, needed):
+    """(status, evicted, loaded, kv_moved) without raising: ENOMEM reports
+    what the step did before it ran out of room."""
+    routed = np.ascontiguousarray(routed, dtype=np.int32)
+    needed = np.ascontiguousarray(needed, dtype=np.uint8)
+    if routed.shape != (adj.E,) or needed.shape != (adj.E,):
+        raise ValueError("routed and needed must have E entries")
+    ev = np.zeros(adj.E, dtype=np.int32)
+    ld = np.zeros(adj.E, dtype=np.int32)
+    ne, nl, moved = C.c_int32(), C.c_int32(), C.c_int64()
+    st = lib().rimuru_adjuster_step(adj.handle, demand_blocks, routed.ctypes.data, needed.ctypes.data,
+                                    ev.ctypes.data, C.byref(ne), ld.ctypes.data, C.byref(nl),
+                                    C.byref(moved))
+    return st, ev[:ne.value].tolist(), ld[:nl.value].tolist(), moved.value
+
+
+def adjuster_step(adj: Adjuster, demand_blocks: int, routed, needed):
+    """{"evicted", "loaded", "kv_moved"} of one policy step."""
+    st, ev, ld, moved = adjuster_step_status(adj, demand_blocks, routed, needed)
+    check(st, "adjuster_step")
+    return {"evicted": ev, "loaded": ld, "kv_moved": moved}
+
+
+def adjuster_upload_done(adj: Adjuster, e: int) -> None:
+    check(lib().rimuru_adjuster_upload_done(adj.handle, e), "adjuster_upload_done")
+
+
+def adjuster_state(adj: Adjuster):
+    """(resident bool [E], in_flight bool [E], score uint64 [E])."""
+    r = np.zeros(adj.E, dtype=np.uint8)
+    f = np.zeros(adj.E, dtype=np.uint8)
+    s = np.zeros(adj.E, dtype=np.uint64)
+    check(lib().rimuru_adjuster_state(adj.handle, r.ctypes.data, f.ctypes.data, s.ctypes.data),
+          "adjuster_state")
+    return r.astype(bool), f.astype(bool), s
 
 
 # ----------------------------------------------------------------- fused MoE
