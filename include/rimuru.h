@@ -254,6 +254,62 @@ rimuru_status rimuru_adjuster_state(const rimuru_adjuster* adj, uint8_t* residen
                                     uint64_t* score);
 
 /* ------------------------------------------------------------------------ */
+/* Paged decode attention over the KV view                                   */
+/* ------------------------------------------------------------------------ */
+
+/* The second workload on the same pool: decode attention reading the KV
+ * cache where its blocks sit in the KV view (explainer "Rimuru unifies
+ * serving memory", paragraph on moving the fence: 16-token KV blocks through
+ * a block table, cut from expert-sized pages; paper summary, Table 1: one
+ * token's K and V are [2, n_kv_heads, head_dim]).
+ *
+ * KV block layout (bf16, 16 tokens; the pages fix no order inside a block):
+ * K of KV heads 0..n_kv-1, each token-major [16][head_dim], then V of KV
+ * heads 0..n_kv-1, each dim-major [head_dim][16]. block_bytes =
+ * 2 * n_kv * 16 * head_dim * 2 (32 KiB for [2, 4, 128]).
+ *
+ * For request b and query head h (KV head h / (n_q / n_kv)):
+ *   out[b, h] = softmax_t(scale * q[b, h] . K_b[t]) V_b, t < context_lens[b],
+ * accumulated in fp32 (probabilities rounded to bf16 for the second
+ * product), written as bf16; context length 0 gives zeros. */
+typedef struct {
+  int32_t B;               /* requests (one query token each), >= 0 */
+  int32_t n_q;             /* query heads: a multiple of n_kv, <= 16 * n_kv */
+  int32_t n_kv;            /* KV heads, >= 1 */
+  int32_t head_dim;        /* 128 or 256 */
+  int32_t max_blocks;      /* columns of block_table, >= 1 */
+  float scale;             /* softmax scale (> 0), e.g. 1/sqrt(head_dim) */
+  const void* q;           /* device bf16 [B, n_q, head_dim], 16-byte aligned */
+  const void* pool_base;   /* device pool, 256-byte aligned */
+  const int32_t* block_table; /* device [B, max_blocks]: block indices in units
+                              of block_bytes from pool_base (the KV view's
+                              page offsets / block_bytes); entries past a
+                              request's context are not read. Not checked on
+                              the device: rimuru_block_table_check checks a
+                              host copy. */
+  const int32_t* context_lens; /* device [B], 0 .. 16 * max_blocks (clamped) */
+  void* out;               /* device bf16 [B, n_q, head_dim] */
+  void* workspace;         /* device, 16-byte aligned, workspace_bytes from
+                              rimuru_attn_sizes; partials of the splits */
+  uint64_t workspace_bytes;
+} rimuru_attn_args;
+
+/* Workspace bytes, number of context splits and block bytes for a shape.
+ * Any output may be NULL. Errors: EINVAL (unsupported shape). */
+rimuru_status rimuru_attn_sizes(int32_t B, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t max_blocks,
+                                uint64_t* workspace_bytes, int32_t* n_split, uint64_t* block_bytes);
+
+/* Enqueue the attention (two kernels: the splits, then their merge) on the
+ * stream; returns without a host sync. Errors: EINVAL, EHIP. */
+rimuru_status rimuru_paged_decode_attention(const rimuru_attn_args* args, void* hip_stream);
+
+/* Host check of a host copy of block_table and context_lens: every block a
+ * request's context covers lies inside a pool of pool_bytes. ERANGE names the
+ * first bad entry or length. */
+rimuru_status rimuru_block_table_check(const int32_t* block_table, int32_t B, int32_t max_blocks,
+                                       const int32_t* context_lens, uint64_t block_bytes, uint64_t pool_bytes);
+
+/* ------------------------------------------------------------------------ */
 /* Page-table-aware fused MoE                                               */
 /* ------------------------------------------------------------------------ */
 

@@ -39,6 +39,13 @@ class AdjusterParams(C.Structure):
                 ("max_prefetch", C.c_int32)]
 
 
+class AttnArgs(C.Structure):
+    _fields_ = [("B", C.c_int32), ("n_q", C.c_int32), ("n_kv", C.c_int32), ("head_dim", C.c_int32),
+                ("max_blocks", C.c_int32), ("scale", C.c_float), ("q", C.c_void_p), ("pool_base", C.c_void_p),
+                ("block_table", C.c_void_p), ("context_lens", C.c_void_p), ("out", C.c_void_p),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64)]
+
+
 class MoeArgs(C.Structure):
     _fields_ = [("T", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("H", C.c_int32),
                 ("I", C.c_int32), ("P", C.c_int32), ("dtype", C.c_int32),
@@ -86,6 +93,11 @@ _PROTOS = {
                                          C.c_void_p, C.c_uint64, C.c_void_p]),
     "rimuru_expert_upload": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_int32, C.c_uint64,
                                          C.c_void_p, C.c_uint64, C.c_void_p]),
+    "rimuru_attn_sizes": (C.c_int32, [C.c_int32] * 5 + [C.POINTER(C.c_uint64), C.POINTER(C.c_int32),
+                                                        C.POINTER(C.c_uint64)]),
+    "rimuru_paged_decode_attention": (C.c_int32, [C.POINTER(AttnArgs), C.c_void_p]),
+    "rimuru_block_table_check": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_uint64,
+                                             C.c_uint64]),
     "rimuru_event_create": (C.c_int32, [C.POINTER(C.c_void_p)]),
     "rimuru_event_destroy": (C.c_int32, [C.c_void_p]),
     "rimuru_event_record": (C.c_int32, [C.c_void_p, C.c_void_p]),

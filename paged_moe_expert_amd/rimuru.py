@@ -9,8 +9,8 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, AdjusterParams,  # noqa: F401
-                   MoeArgs, OK, PoolStats, RimuruError, check, lib)
+from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, ERANGE, AdjusterParams,  # noqa: F401
+                   AttnArgs, MoeArgs, OK, PoolStats, RimuruError, check, lib)
 
 
 # ----------------------------------------------------------------- pool and views
@@ -304,6 +304,48 @@ def expert_upload(pool, pt_rows, page_bytes: int, host, stream=None) -> None:
     s = stream if stream is not None else torch.cuda.current_stream(pool.device)
     check(expert_upload_raw(pool.data_ptr(), pool.numel() * pool.element_size(), pt_rows, page_bytes,
                             host.data_ptr(), proj_bytes, s.cuda_stream), "expert_upload")
+
+
+# ----------------------------------------------------------------- paged decode attention
+
+def attn_sizes(B: int, n_q: int, n_kv: int, head_dim: int, max_blocks: int):
+    """(workspace_bytes, n_split, block_bytes)."""
+    ws, ns, bb = C.c_uint64(), C.c_int32(), C.c_uint64()
+    check(lib().rimuru_attn_sizes(B, n_q, n_kv, head_dim, max_blocks, C.byref(ws), C.byref(ns), C.byref(bb)),
+          "attn_sizes")
+    return ws.value, ns.value, bb.value
+
+
+def block_table_check(block_table, context_lens, block_bytes: int, pool_bytes: int) -> None:
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    check(lib().rimuru_block_table_check(bt.ctypes.data, bt.shape[0], bt.shape[1], lens.ctypes.data,
+                                         block_bytes, pool_bytes), "block_table_check")
+
+
+def paged_decode_attention(q, pool, block_table, context_lens, n_kv: int, scale: float, out=None,
+                           workspace=None, stream=None):
+    """q bf16 [B, n_q, head_dim]; pool uint8 device tensor; block_table int32
+    [B, max_blocks] and context_lens int32 [B] on the device. Returns out
+    (bf16 [B, n_q, head_dim]); enqueued on stream (default: current)."""
+    import torch
+    B, n_q, D = q.shape
+    max_blocks = block_table.shape[1]
+    ws, _, _ = attn_sizes(B, n_q, n_kv, D, max_blocks)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise RimuruError(-4, "paged_decode_attention", "q and out must be bf16")
+    for t in (q, block_table, context_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("paged_decode_attention: tensors must be contiguous")
+    a = AttnArgs(B, n_q, n_kv, D, max_blocks, scale, q.data_ptr(), pool.data_ptr(), block_table.data_ptr(),
+                 context_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel())
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    check(lib().rimuru_paged_decode_attention(C.byref(a), s.cuda_stream), "paged_decode_attention")
+    return out
 
 
 # ----------------------------------------------------------------- timing helpers
