@@ -200,6 +200,77 @@ def expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np):
             "rounds_overlapped": rounds}
 
 
+def attention_bench(args, cfg, lay, pool, dev, R, torch, np):
+    """Paged decode attention over the KV view of the layer's own pool: the
+    first n live KV requests of the layout (their blocks sit between the
+    expert pages), one query token each, K/V filled with N(0, 1) bf16 and
+    contexts of (blocks - u) tokens, u ~ U{0..15} seeded. Timed back to back
+    (a batch of calls between two events) and cache-cold (a 4 GiB read before
+    each call, an event pair around it)."""
+    ks = cfg.view("kv")
+    bb = ks.page_bytes
+    n_kv, D = cfg.kv_shape[1], cfg.kv_shape[2]
+    n_q = 8 * n_kv                                   # Qwen3-30B-A3B: 32 query heads over 4 KV heads
+    kv = lay.views["kv"]
+    reqs = [o for name, o in lay.live if name == "kv"][:args.attn_requests]
+    blocks = [R.view_pages(kv, o) // bb for o in reqs]
+    B, mb = len(blocks), max(len(b) for b in blocks)
+    rng = np.random.default_rng(2024)
+    lens = np.array([16 * len(b) - int(rng.integers(0, 16)) for b in blocks], dtype=np.int32)
+    table = np.zeros((B, mb), dtype=np.int32)
+    for i, b in enumerate(blocks):
+        table[i, :len(b)] = b
+    R.block_table_check(table, lens, bb, cfg.pool_bytes)
+    idx = torch.from_numpy(np.concatenate(blocks).astype(np.int64)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2025)
+    kvv = pool.view(torch.bfloat16).view(-1, bb // 2)
+    kvv[idx] = torch.randn((idx.numel(), bb // 2), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((B, n_q, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bt = torch.from_numpy(table).to(dev)
+    lt = torch.from_numpy(lens).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes, n_split, _ = R.attn_sizes(B, n_q, n_kv, D, mb)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+
+    def call():
+        R.paged_decode_attention(q, pool, bt, lt, n_kv, scale, out=out, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = R.event_create(), R.event_create()
+    R.event_record(e0)
+    for _ in range(args.steps):
+        call()
+    R.event_record(e1)
+    torch.cuda.synchronize()
+    warm_us = R.event_elapsed_ms(e0, e1) * 1e3 / args.steps
+    flush = torch.ones((4096 << 20) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        torch.sum(flush, dim=0, out=sink)
+        R.event_record(e0)
+        call()
+        R.event_record(e1)
+        torch.cuda.synchronize()
+        cold.append(R.event_elapsed_ms(e0, e1) * 1e3)
+    del flush
+    R.event_destroy(e0)
+    R.event_destroy(e1)
+    kv_bytes = int(lens.sum()) * 2 * n_kv * D * 2
+    io_bytes = 2 * B * n_q * D * 2 + B * (mb + 1) * 4
+    cold_us = float(np.median(cold))
+    return {"requests": B, "n_q": n_q, "n_kv": n_kv, "head_dim": D, "context_tokens": int(lens.sum()),
+            "context_min_max": [int(lens.min()), int(lens.max())], "splits": int(n_split),
+            "algorithmic_bytes": kv_bytes + io_bytes,
+            "us_per_call_back_to_back": round(warm_us, 2),
+            "us_per_call_cache_cold_median": round(cold_us, 2),
+            "hbm_gbs_cache_cold": round((kv_bytes + io_bytes) / (cold_us * 1e-6) / 1e9, 1),
+            "hbm_frac_cache_cold": round((kv_bytes + io_bytes) / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +286,8 @@ def main():
                     help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
     ap.add_argument("--no-adjuster", action="store_true",
                     help="skip the host-side adjuster policy measurement")
+    ap.add_argument("--attn-requests", type=int, default=256,
+                    help="decode-attention requests taken from the layout's KV view (0: skip)")
     ap.add_argument("--no-router", action="store_true",
                     help="skip the run that computes the router projection in the gating stage")
     ap.add_argument("--no-contiguous", action="store_true",
@@ -248,7 +321,8 @@ def main():
 
     # ---- layout and device-resident inputs (untimed)
     t0 = time.perf_counter()
-    pt = DeviceLayout(cfg).run().page_table()
+    lay = DeviceLayout(cfg).run()
+    pt = lay.page_table()
     wb = gen.all_weight_bits(cfg)
     xb, lg = gen.x_bits(cfg, T), gen.logits(cfg, T)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -379,6 +453,12 @@ def main():
     if args.upload_experts:
         upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
+    # Timed region 6: paged decode attention over the same pool's KV view.
+    attn = None
+    if args.attn_requests and cfg.dtype == "bf16" and any(v.name == "kv" for v in cfg.views) \
+            and any(name == "kv" for name, _ in lay.live):
+        attn = attention_bench(args, cfg, lay, pool, dev, R, torch, np)
+
     if args.copy_calibration:
         n = args.copy_calibration << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -459,6 +539,8 @@ def main():
     if not args.no_adjuster and any(v.name == "kv" and v.parent == "expert" for v in cfg.views):
         gbs = upload["upload_gbs_alone"] if upload is not None else None
         out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
+    if attn is not None:
+        out["attention"] = attn
     if router is not None:
         router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
         out["with_router"] = router

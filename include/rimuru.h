@@ -234,7 +234,7 @@ rimuru_status rimuru_adjuster_destroy(rimuru_adjuster* adj); /* NULL is a no-op 
  *   routed         host int32 [E] routed slots per expert in the last step
  *                  (>= 0), or NULL for none.
  *   needed         host uint8 [E], nonzero = the next layer call reads the expert.
- *   evicted, loaded  host int32 arrays of capacity E; *n_evicted/*n_loaded
+ *   evicted, loaded  host int32 arrays of capacity E; *n_evicted and *n_loaded
  *                  receive the counts (an expert appears at most once in each).
  *   kv_moved       bytes of budget moved toward the KV view (negative: toward
  *                  the experts), net over the step; may be NULL.

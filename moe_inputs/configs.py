@@ -62,6 +62,7 @@ class MoEConfig:
     n_events: int = 0          # churn events (fragmented recipe)
     batches: tuple = ()        # decode sweep batch sizes
     adjuster_steps: int = 0
+    kv_shape: tuple = ()       # one token's K and V: [2, kv_heads, head_dim] (Table 1)
 
     @property
     def es(self) -> int:
@@ -107,7 +108,7 @@ CFG1 = MoEConfig(
     page_bytes=4 * KIB, huge_bytes=lcm(4 * KIB, _c1_kv), pool_bytes=256 * 4 * KIB,
     logits="normal",
     views=(ViewSpec("expert", 0, 4 * KIB, None), ViewSpec("kv", 1, _c1_kv, None)),
-    layout="scatter",
+    layout="scatter", kv_shape=(2, 4, 32),
 )
 
 # Qwen3-30B-A3B decode: one 3 MiB page per projection; KV block 16 x [2,4,128]
@@ -118,7 +119,7 @@ CFG2 = MoEConfig(
     page_bytes=3 * MIB, huge_bytes=lcm(3 * MIB, _q3_kv), pool_bytes=4 * GIB,
     logits="uniform",
     views=(ViewSpec("expert", 0, 3 * MIB, None), ViewSpec("kv", 1, _q3_kv, "expert")),
-    layout="fill_then_place",
+    layout="fill_then_place", kv_shape=(2, 4, 128),
 )
 
 # Qwen3.5-35B-A3B prefill: 2 MiB projections; SSM state [32,128,128] bf16 = 1 MiB;
@@ -133,7 +134,7 @@ CFG3 = MoEConfig(
     logits="zipf", zipf_s=1.1,
     views=(ViewSpec("expert", 0, 2 * MIB, None), ViewSpec("kv", 1, _q35_kv, "expert"),
            ViewSpec("ssm", 2, _q35_ssm, None), ViewSpec("conv", 3, _q35_conv, "expert")),
-    layout="fill_then_place",
+    layout="fill_then_place", kv_shape=(2, 2, 256),
 )
 
 # Large prefill with sub-page fragmentation: 64 KiB expert pages (48 per
@@ -144,7 +145,7 @@ CFG4 = MoEConfig(
     page_bytes=64 * KIB, huge_bytes=3 * MIB, pool_bytes=4 * GIB,
     logits="zipf", zipf_s=1.2,
     views=(ViewSpec("expert", 0, 64 * KIB, None), ViewSpec("kv", 1, _q3_kv, "expert")),
-    layout="churn", n_events=10_000,
+    layout="churn", n_events=10_000, kv_shape=(2, 4, 128),
 )
 
 # Decode sweep under a moving KV/expert boundary: the decode layout, then
@@ -154,7 +155,7 @@ CFG5 = MoEConfig(
     page_bytes=3 * MIB, huge_bytes=lcm(3 * MIB, _q3_kv), pool_bytes=4 * GIB,
     logits="uniform",
     views=(ViewSpec("expert", 0, 3 * MIB, None), ViewSpec("kv", 1, _q3_kv, "expert")),
-    layout="fill_then_place", batches=(1, 4, 16, 64, 256), adjuster_steps=10,
+    layout="fill_then_place", batches=(1, 4, 16, 64, 256), adjuster_steps=10, kv_shape=(2, 4, 128),
 )
 
 CONFIGS = {c.cid: c for c in (CFG1, CFG2, CFG3, CFG4, CFG5)}
