@@ -271,7 +271,9 @@ rimuru_status rimuru_adjuster_state(const rimuru_adjuster* adj, uint8_t* residen
  * For request b and query head h (KV head h / (n_q / n_kv)):
  *   out[b, h] = softmax_t(scale * q[b, h] . K_b[t]) V_b, t < context_lens[b],
  * accumulated in fp32 (probabilities rounded to bf16 for the second
- * product), written as bf16; context length 0 gives zeros. */
+ * product), written as bf16; context length 0 gives zeros. Token slots past
+ * the context in a request's last block get probability 0 but are still
+ * multiplied, so they must hold finite values (0 * NaN is NaN). */
 typedef struct {
   int32_t B;               /* requests (one query token each), >= 0 */
   int32_t n_q;             /* query heads: a multiple of n_kv, <= 16 * n_kv */
