@@ -301,7 +301,9 @@ typedef struct {
 rimuru_status rimuru_attn_sizes(int32_t B, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t max_blocks,
                                 uint64_t* workspace_bytes, int32_t* n_split, uint64_t* block_bytes);
 
-/* Enqueue the attention (two kernels: the splits, then their merge) on the
+/* Enqueue the attention (two kernels: the splits, then their merge; the
+ * first alone when every context fits one split, e.g. 256 or more requests
+ * over 4 KV heads) on the
  * stream; returns without a host sync. Errors: EINVAL, EHIP. */
 rimuru_status rimuru_paged_decode_attention(const rimuru_attn_args* args, void* hip_stream);
 

@@ -20,6 +20,7 @@
 // too, so the online-softmax state of head h lives on the lanes h, h+16,
 // h+32, h+48 and rescaling needs no data movement. G < 16 pads q with zeros.
 // Splits write unnormalised partials (O, m, l); a second kernel merges them.
+// With a single split the first kernel normalises and writes the output.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -33,6 +34,8 @@ namespace {
 constexpr int kBT = 16;        // tokens per KV block
 constexpr int kWaves = 4;
 constexpr int kMinWorkgroups = 1024;
+constexpr int kMaxChunk = 1024;  // blocks per split: the split's block-table slice fits LDS
+constexpr int kRound = 2;        // blocks a wavefront loads per round
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) {
   return __shfl_xor(v, m, 64);
@@ -103,14 +106,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_paged_attn(const uint16_t* __re
                                                             const int32_t* __restrict__ ctx_lens, int n_q,
                                                             int n_kv, int max_blocks, int chunk, int n_split,
                                                             float scale_log2, float* __restrict__ part_o,
-                                                            float* __restrict__ part_ml) {
+                                                            float* __restrict__ part_ml,
+                                                            uint16_t* __restrict__ out) {
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = n_q / n_kv;
   const int L = min(max(ctx_lens[b], 0), max_blocks * kBT);
   const int nblk = (L + kBT - 1) / kBT;
   const int blk0 = split * chunk, blk1 = min(blk0 + chunk, nblk);
-  if (blk0 >= blk1) return;       // nothing of this request in this split
+  if (blk0 >= blk1) {             // nothing of this request in this split
+    if (out != nullptr) {         // one split: an empty context gives zeros
+      const int G0 = n_q / n_kv;
+      uint16_t* o = out + (static_cast<int64_t>(b) * n_q + j * G0) * D;
+      for (int i = threadIdx.x; i < G0 * D; i += kWaves * 64) o[i] = 0;
+    }
+    return;
+  }
   const uint64_t bbytes = static_cast<uint64_t>(2) * n_kv * kBT * D * 2;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_blocks;
 
@@ -131,15 +142,26 @@ __global__ __launch_bounds__(kWaves * 64) void k_paged_attn(const uint16_t* __re
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // blocks blk0 + w, + 4, ... two per round; the second of a pair past the
-  // range re-reads the first and is skipped
-  for (int i = blk0 + w; i < blk1; i += 2 * kWaves) {
-    const int i2 = i + kWaves < blk1 ? i + kWaves : i;
-    AttnFrags<D> fa, fb;
-    load_block<D>(fa, pool + static_cast<uint64_t>(bt[i]) * bbytes, j, n_kv, lane);
-    load_block<D>(fb, pool + static_cast<uint64_t>(bt[i2]) * bbytes, j, n_kv, lane);
-    attend_block<D>(st, fa, qf, i * kBT, L, scale_log2, lane);
-    if (i2 != i) attend_block<D>(st, fb, qf, i2 * kBT, L, scale_log2, lane);
+  // The split's block indices, staged in LDS once: a block's address is then
+  // an LDS read away instead of a dependent global load per round.
+  __shared__ int32_t sbt[kMaxChunk];
+  for (int i = threadIdx.x; i < blk1 - blk0; i += kWaves * 64) sbt[i] = bt[blk0 + i];
+  __syncthreads();
+
+  // blocks blk0 + w, + 4, ... kRound per round, all loaded before the first
+  // is multiplied; a block past the range re-reads the round's first and is
+  // skipped
+  for (int i = blk0 + w; i < blk1; i += kRound * kWaves) {
+    AttnFrags<D> f[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int iu = i + u * kWaves < blk1 ? i + u * kWaves : i;
+      load_block<D>(f[u], pool + static_cast<uint64_t>(sbt[iu - blk0]) * bbytes, j, n_kv, lane);
+    }
+    attend_block<D>(st, f[0], qf, i * kBT, L, scale_log2, lane);
+#pragma unroll
+    for (int u = 1; u < kRound; ++u)
+      if (i + u * kWaves < blk1) attend_block<D>(st, f[u], qf, (i + u * kWaves) * kBT, L, scale_log2, lane);
   }
   st.l += wave_shfl_xor(st.l, 16);
   st.l += wave_shfl_xor(st.l, 32);
@@ -170,6 +192,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_paged_attn(const uint16_t* __re
     l += av * sl[v][lane];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) st.o[c] += av * so[v][c][lane];
+  }
+  if (out != nullptr) {
+    // one split: normalise and write the output here (the merge kernel would
+    // scale by 2^0 = 1 and divide the same values)
+    if (h < G) {
+      uint16_t* po = out + (static_cast<int64_t>(b) * n_q + j * G + h) * D + 4 * (lane >> 4);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[16 * c + r] = static_cast<uint16_t>(f32_to_bf16(st.o[c][r] / l));
+    }
+    return;
   }
   if (h < G) {
     const int64_t r = ((static_cast<int64_t>(b) * n_q + j * G + h) * n_split + split);
@@ -208,8 +242,10 @@ int pick_split(int B, int n_kv, int max_blocks) {
   const int64_t pairs = static_cast<int64_t>(B) * n_kv;
   if (pairs == 0) return 1;
   int ns = static_cast<int>((kMinWorkgroups + pairs - 1) / pairs);
-  const int most = (max_blocks + 2 * kWaves - 1) / (2 * kWaves);   // at least one round per wavefront
+  const int most = (max_blocks + kRound * kWaves - 1) / (kRound * kWaves);   // at least one round per wavefront
   if (ns > most) ns = most;
+  const int fewest = (max_blocks + kMaxChunk - 1) / kMaxChunk;     // each split's table fits LDS
+  if (ns < fewest) ns = fewest;
   return ns < 1 ? 1 : ns;
 }
 
@@ -222,9 +258,9 @@ hipError_t launch_attn(const rimuru_attn_args* a, int n_split, hipStream_t st) {
   hipLaunchKernelGGL(k_paged_attn<D>, dim3(n_split, a->n_kv, a->B), dim3(kWaves * 64), 0, st,
                      static_cast<const uint16_t*>(a->q), static_cast<const uint8_t*>(a->pool_base),
                      a->block_table, a->context_lens, a->n_q, a->n_kv, a->max_blocks, chunk, n_split,
-                     scale_log2, part_o, part_ml);
+                     scale_log2, part_o, part_ml, n_split == 1 ? static_cast<uint16_t*>(a->out) : nullptr);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || n_split == 1) return err;
   hipLaunchKernelGGL(k_attn_merge<D>, dim3(a->B * a->n_q), dim3(D), 0, st, part_o, part_ml, a->context_lens,
                      a->n_q, a->max_blocks, chunk, n_split, static_cast<uint16_t*>(a->out));
   return hipGetLastError();

@@ -123,6 +123,25 @@ def test_group_ratios(n_q, n_kv):
     run_case([7, 48, 300, 1], n_q, n_kv, 128, seed=4 + n_q)
 
 
+def test_context_beyond_one_split_table():
+    """A context of 1100 blocks among many short requests: the split count is
+    raised so that no split's block-table slice exceeds 1024 blocks."""
+    lens = [17600] + [5] * 299
+    ns = run_case(lens, 32, 4, 128, seed=11, sample=[0, 1, 150, 299])
+    assert ns >= 2
+
+
+def test_single_split_writes_output_directly():
+    """256 requests over 4 KV heads take one split: the first kernel writes
+    the normalised output itself (no merge launch), empty contexts included."""
+    rng = np.random.default_rng(12)
+    lens = np.clip(np.rint(rng.lognormal(4.5, 1.0, 256)), 1, 700).astype(int)
+    lens[[3, 100, 255]] = 0
+    lens = lens.tolist()
+    ns = run_case(lens, 32, 4, 128, seed=13, sample=[0, 3, 7, 100, 128, 200, 255], expert_every=8)
+    assert ns == 1
+
+
 def test_no_requests_is_a_no_op():
     dev = torch.device("cuda:0")
     q = torch.zeros((0, 32, 128), dtype=torch.bfloat16, device=dev)
