@@ -271,6 +271,58 @@ def attention_bench(args, cfg, lay, pool, dev, R, torch, np):
             "hbm_frac_cache_cold": round((kv_bytes + io_bytes) / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def copy_foil_bench(args, cfg, x, lgd, pool, ptd, pt, bufs, dev, R, torch, np):
+    """The copy the paged kernel avoids: each step first gathers every touched
+    expert's pages into one contiguous buffer (one device gather of whole
+    pages), then runs the same layer on that buffer. The touched set is the
+    one this input routes to (the same every step)."""
+    off = bufs.expert_off.cpu().numpy()
+    srt = bufs.sorted_ids.cpu().numpy()
+    TK = x.shape[0] * cfg.k
+    touched = [e for e in range(cfg.E) if np.any(srt[off[e]:off[e + 1]] < TK)]
+    pages = np.ascontiguousarray(pt[touched].reshape(-1)).astype(np.int64)   # [touched][3][P] pool pages
+    staged_pt = np.zeros_like(pt)
+    staged_pt[touched] = np.arange(pages.size, dtype=np.int32).reshape(len(touched), 3, cfg.P)
+    idx = torch.from_numpy(pages).to(dev)
+    whole = cfg.pool_bytes // cfg.page_bytes * (cfg.page_bytes // 8)     # the pool's whole pages
+    src = pool.view(torch.int64)[:whole].view(-1, cfg.page_bytes // 8)
+    staged = torch.empty((pages.size, cfg.page_bytes // 8), dtype=torch.int64, device=dev)
+    spt = torch.from_numpy(staged_pt).to(dev)
+    sview = staged.view(torch.uint8).view(-1)
+
+    def gather():
+        torch.index_select(src, 0, idx, out=staged)
+
+    def fstep():
+        gather()
+        R.fused_moe_paged(x, lgd, sview, spt, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
+    ybuf = bufs.y.clone()
+    fstep()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ybuf.view(torch.uint8), bufs.y.view(torch.uint8)))
+    for _ in range(args.warmup):
+        fstep()
+    e0, e1, e2 = R.event_create(), R.event_create(), R.event_create()
+    torch.cuda.synchronize()
+    R.event_record(e0)
+    for _ in range(args.steps):
+        fstep()
+    R.event_record(e1)
+    for _ in range(args.steps):
+        gather()
+    R.event_record(e2)
+    torch.cuda.synchronize()
+    step_ms = R.event_elapsed_ms(e0, e1) / args.steps
+    gather_ms = R.event_elapsed_ms(e1, e2) / args.steps
+    for e in (e0, e1, e2):
+        R.event_destroy(e)
+    moved = 2 * pages.size * cfg.page_bytes
+    del staged
+    return {"experts_gathered": len(touched), "bytes_gathered": int(pages.size * cfg.page_bytes),
+            "gather_ms": round(gather_ms, 4), "gather_gbs_read_plus_write": round(moved / (gather_ms * 1e-3) / 1e9, 1),
+            "ms_per_step_gather_then_layer": round(step_ms, 4), "bitwise_equal_output": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +340,8 @@ def main():
                     help="skip the host-side adjuster policy measurement")
     ap.add_argument("--attn-requests", type=int, default=256,
                     help="decode-attention requests taken from the layout's KV view (0: skip)")
+    ap.add_argument("--no-foil", action="store_true",
+                    help="skip the gather-then-contiguous foil (the copy the paged kernel avoids)")
     ap.add_argument("--no-router", action="store_true",
                     help="skip the run that computes the router projection in the gating stage")
     ap.add_argument("--no-contiguous", action="store_true",
@@ -453,6 +507,11 @@ def main():
     if args.upload_experts:
         upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
+    # Timed region 7: the foil -- gather the touched experts, then the layer.
+    foil = None
+    if not args.no_foil:
+        foil = copy_foil_bench(args, cfg, x, lgd, pool, ptd, pt, bufs, dev, R, torch, np)
+
     # Timed region 6: paged decode attention over the same pool's KV view.
     attn = None
     if args.attn_requests and cfg.dtype == "bf16" and any(v.name == "kv" for v in cfg.views) \
@@ -541,6 +600,9 @@ def main():
         out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
     if attn is not None:
         out["attention"] = attn
+    if foil is not None:
+        foil["foil_over_paged"] = round(foil["ms_per_step_gather_then_layer"] / ms_step, 3)
+        out["copy_foil"] = foil
     if router is not None:
         router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
         out["with_router"] = router
