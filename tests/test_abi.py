@@ -143,3 +143,51 @@ def test_expert_upload_validates_before_copying():
     assert "projection 2, page 3" in _lib.lib().rimuru_last_error().decode()
     bad[2, 3] = -1
     assert status(pt_rows=bad) == _lib.ERANGE
+
+
+def _attn_args(**over):
+    base = dict(B=2, n_q=32, n_kv=4, head_dim=128, max_blocks=4, scale=0.125, q=1 << 20,
+                pool_base=1 << 21, block_table=1 << 22, context_lens=1 << 23, out=1 << 24,
+                workspace=1 << 25, workspace_bytes=1 << 30)
+    base.update(over)
+    return _lib.AttnArgs(*[base[f] for f, _ in _lib.AttnArgs._fields_])
+
+
+@pytest.mark.parametrize("over", [
+    dict(head_dim=64), dict(n_q=30), dict(n_q=68), dict(n_kv=0), dict(max_blocks=0), dict(scale=0.0),
+    dict(scale=float("inf")), dict(q=0), dict(workspace=0), dict(q=(1 << 20) + 8),
+    dict(pool_base=(1 << 21) + 128), dict(workspace_bytes=16), dict(B=-1),
+])
+def test_attention_rejects_bad_arguments_without_launching(over):
+    a = _attn_args(**over)
+    assert _lib.lib().rimuru_paged_decode_attention(C.byref(a), None) == _lib.EINVAL
+
+
+def test_attention_no_requests_is_a_noop_and_split_choice():
+    a = _attn_args(B=0, q=0, out=0)
+    assert _lib.lib().rimuru_paged_decode_attention(C.byref(a), None) == _lib.OK
+    # one split once B * n_kv fills 1024 workgroups; more for few requests;
+    # never a split longer than 1024 blocks
+    assert R.attn_sizes(256, 32, 4, 128, 127)[1] == 1
+    assert R.attn_sizes(1, 32, 4, 128, 256)[1] == 32
+    assert R.attn_sizes(300, 32, 4, 128, 1100)[1] == 2
+    ws, ns, bb = R.attn_sizes(3, 16, 2, 256, 10)
+    assert bb == 2 * 2 * 16 * 256 * 2 and ws == 3 * 16 * ns * (256 + 2) * 4
+
+
+def test_block_table_check_names_bad_entries():
+    table = np.array([[0, 1, 2], [3, 9, 0]], dtype=np.int32)
+    R.block_table_check(table, np.array([48, 17], dtype=np.int32), 4096, 10 * 4096)
+    with pytest.raises(R.RimuruError, match="ERANGE"):
+        R.block_table_check(table, np.array([48, 33], dtype=np.int32), 4096, 9 * 4096)   # block 9 outside
+    with pytest.raises(R.RimuruError, match="ERANGE"):
+        R.block_table_check(table, np.array([49, 1], dtype=np.int32), 4096, 10 * 4096)   # 4 blocks > 3
+
+
+def test_bench_is_one_gpu_only():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
