@@ -209,6 +209,13 @@ def test_full_size_configs(cid, n_sample):
     assert torch.equal(cc.y, y0), "paged and contiguous layouts differ"
     again = c.run()
     assert torch.equal(again.y, y0), "run-to-run difference"
+    if cfg.P > 1:
+        # the same weights with one page per projection (page = the whole
+        # projection): another page size, the same bytes, the same output
+        pt1 = torch.from_numpy(np.arange(cfg.E * 3, dtype=np.int32).reshape(cfg.E, 3, 1)).cuda()
+        one = R.fused_moe_paged(c.x, c.lgd, c.wdev.view(torch.uint8).reshape(-1), pt1, cfg.proj_bytes, cfg.k, cfg.I)
+        torch.cuda.synchronize()
+        assert torch.equal(one.y, y0), "one page per projection differs from the paged layout"
 
 
 @pytest.mark.timeout(900)
