@@ -120,6 +120,30 @@ def test_custom_shapes_against_oracle(spec):
     assert torch.equal(b2.y, bufs.y)
 
 
+@pytest.mark.parametrize("T", [8, 40], ids=["one-workgroup-routing", "gating-and-sort"])
+def test_tied_and_signed_zero_logits(T):
+    """Logits drawn from {-1, -0.0, +0.0, 0.5, 1} (seeded): most tokens have
+    ties at the top-k boundary and between -0 and +0. The kernels must keep
+    the lower expert index on a tie and treat -0 as +0, exactly as the
+    oracle's route does."""
+    E, k, H, I, page = 16, 4, 256, 128, 4 * KIB
+    name = f"bf16-ties-T{T}"
+    cfg, P, n_pages, pt, wb, xb, _ = _custom(name, E, k, H, I, T, "bf16", page, seed=50 + T)
+    r = np.random.default_rng(77 + T)
+    lg = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], dtype=np.float32)[r.integers(0, 5, size=(T, E))]
+    assert np.signbit(lg).any() and (lg == 0).any()
+    wdev = weights_dev(_padded_weights(wb, P, page))
+    pool, ptd = paged_pool(n_pages * page, pt, wdev, page)
+    x = to_dev_bits(xb, "bf16")
+    bufs = R.fused_moe_paged(x, torch.from_numpy(lg).cuda(), pool, ptd, page, k, I)
+    torch.cuda.synchronize()
+    ref = moe_forward(xb, lg, _ref_pool(n_pages, page, pt, wb, P), pt, page, E=E, k=k, H=H, I=I, dtype="bf16")
+    check_routing(bufs, ref, T, k, E, bufs.block_m)
+    err = rel_err(decode_dev(bufs.y), ref["y"])
+    say(f"[ties] T={T}: rel_err={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- registry configs
 
 @pytest.fixture(scope="module")
