@@ -242,36 +242,43 @@ void launch_router(const RouterArgs& r, int n_tok, int E, hipStream_t st) {
 
 // ids is 16-byte aligned (validated); 8 independent 16-byte loads per thread
 // are in flight per round.
-__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int TK,
-                                               int32_t* __restrict__ counts) {
-  __shared__ int part[4];
+template <int NT>
+__global__ __launch_bounds__(NT) void k_count(const int32_t* __restrict__ ids, int TK,
+                                              int32_t* __restrict__ counts) {
+  __shared__ int part[NT / 64];
   const int e = blockIdx.x;
   const int n4 = TK >> 2;
   const u32x4* v = reinterpret_cast<const u32x4*>(ids);
   const uint32_t ue = static_cast<uint32_t>(e);
   int c = 0;
-  for (int base = 0; base < n4; base += 256 * 8) {
+  for (int base = 0; base < n4; base += NT * 8) {
     u32x4 r[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int i = base + u * 256 + threadIdx.x;
+      const int i = base + u * NT + threadIdx.x;
       r[u] = (i < n4) ? v[i] : u32x4{~0u, ~0u, ~0u, ~0u};
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       c += (r[u][0] == ue) + (r[u][1] == ue) + (r[u][2] == ue) + (r[u][3] == ue);
   }
-  for (int f = n4 * 4 + threadIdx.x; f < TK; f += 256) c += (ids[f] == e);
+  for (int f = n4 * 4 + threadIdx.x; f < TK; f += NT) c += (ids[f] == e);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
   __syncthreads();
-  if (threadIdx.x == 0) counts[e] = part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0) {
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) sum += part[i];
+    counts[e] = sum;
+  }
 }
 
 // ---------------------------------------------------------------- stage 3: sort + align
 
-// Exclusive prefix of v over the 256 threads of the block; *total gets the sum.
+// Exclusive prefix of v over the NT threads of the block; *total gets the sum.
+template <int NT = 256>
 __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl = v;
@@ -284,7 +291,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     before += (i < wv) ? sh[i] : 0;
     all += sh[i];
   }
@@ -299,33 +306,34 @@ constexpr int kSortChunk = 64;  // consecutive slots per thread per round (16 x 
 // LDS (small batches: this saves the separate count launch).
 constexpr int kSortSelfCountMax = 4096;   // routed slots
 
-__global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
-                                                    int BM, const int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ sorted_ids,
-                                                    int32_t* __restrict__ expert_off,
-                                                    int32_t* __restrict__ tile_expert) {
-  __shared__ int sh[4];
+template <int NT>
+__global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
+                                                   int BM, const int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ sorted_ids,
+                                                   int32_t* __restrict__ expert_off,
+                                                   int32_t* __restrict__ tile_expert) {
+  __shared__ int sh[NT / 64];
   __shared__ int hist[kMaxE];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const uint32_t ue = static_cast<uint32_t>(e);
   if (counts == nullptr) {
-    for (int i = tid; i < E; i += 256) hist[i] = 0;
+    for (int i = tid; i < E; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int f = tid; f < TK; f += 256) atomicAdd(&hist[ids[f]], 1);
+    for (int f = tid; f < TK; f += NT) atomicAdd(&hist[ids[f]], 1);
     __syncthreads();
     counts = hist;
   }
   // start of this expert's padded segment, and the padded total
   int before = 0, total = 0;
-  for (int e2 = tid; e2 < E; e2 += 256) {
+  for (int e2 = tid; e2 < E; e2 += NT) {
     int pc = (counts[e2] + BM - 1) / BM * BM;
     total += pc;
     before += (e2 < e) ? pc : 0;
   }
   int sum_before, sum_total;
-  block_excl_scan(before, &sum_before, sh);   // block sums of the per-thread partials
-  block_excl_scan(total, &sum_total, sh);
+  block_excl_scan<NT>(before, &sum_before, sh);   // block sums of the per-thread partials
+  block_excl_scan<NT>(total, &sum_total, sh);
   const int seg = sum_before;
   const int cnt = counts[e];
   if (tid == 0) {
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ 
   }
   const bool vec = (TK & 3) == 0;
   int running = 0;
-  for (int base = 0; base < TK; base += 256 * kSortChunk) {
+  for (int base = 0; base < TK; base += NT * kSortChunk) {
     const int f0 = base + tid * kSortChunk;
     uint64_t mask = 0;
     if (vec) {
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ 
       }
     }
     int chunk_total;
-    int pos = seg + running + block_excl_scan(__popcll(mask), &chunk_total, sh);
+    int pos = seg + running + block_excl_scan<NT>(__popcll(mask), &chunk_total, sh);
     while (mask) {
       const int i = __ffsll(static_cast<long long>(mask)) - 1;
       sorted_ids[pos++] = f0 + i;
@@ -363,8 +371,8 @@ __global__ __launch_bounds__(256) void k_sort_align(const int32_t* __restrict__ 
     running += chunk_total;
   }
   const int padded = (cnt + BM - 1) / BM * BM;
-  for (int i = cnt + tid; i < padded; i += 256) sorted_ids[seg + i] = TK;
-  for (int i = tid; i < padded / BM; i += 256) tile_expert[seg / BM + i] = e;
+  for (int i = cnt + tid; i < padded; i += NT) sorted_ids[seg + i] = TK;
+  for (int i = tid; i < padded / BM; i += NT) tile_expert[seg / BM + i] = e;
 }
 
 // ---------------------------------------------------------------- stages 1-3 for small batches
@@ -557,12 +565,18 @@ hipError_t launch_routing(const float* logits, const RouterArgs* router, int T, 
   if ((err = mark(1)) != hipSuccess) return err;
   const bool self_count = TK <= kSortSelfCountMax;
   if (!self_count) {
-    hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, st, topk_ids, TK, counts);
+    // many slots: 1024 threads a workgroup, so each expert's scan over all
+    // slots takes a quarter of the rounds
+    hipLaunchKernelGGL(k_count<1024>, dim3(E), dim3(1024), 0, st, topk_ids, TK, counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if ((err = mark(2)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_sort_align, dim3(E), dim3(256), 0, st, topk_ids, TK, E, bm,
-                     self_count ? nullptr : counts, sorted_ids, expert_off, tile_expert);
+  if (self_count)
+    hipLaunchKernelGGL(k_sort_align<256>, dim3(E), dim3(256), 0, st, topk_ids, TK, E, bm, nullptr, sorted_ids,
+                       expert_off, tile_expert);
+  else
+    hipLaunchKernelGGL(k_sort_align<1024>, dim3(E), dim3(1024), 0, st, topk_ids, TK, E, bm, counts, sorted_ids,
+                       expert_off, tile_expert);
   return hipGetLastError();
 }
 
