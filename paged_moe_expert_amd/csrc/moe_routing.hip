@@ -476,7 +476,10 @@ __global__ __launch_bounds__(kTinyThreads) void k_route_tiny(const float* __rest
 
 // ---------------------------------------------------------------- stage 6: combine
 
-template <typename T>
+// KMAX >= k: all k slot rows are loaded before the first is added (rows past
+// k reload row k-1 and are not added), so a thread waits for one memory
+// round trip instead of k; the sum still runs j = 0 .. k-1 in order.
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ yslot, int k, int H,
                                                  T* __restrict__ y) {
   typedef Elt<T> X;
@@ -487,10 +490,16 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ yslot, in
   float acc[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) acc[c] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    u32x4 s = *reinterpret_cast<const u32x4*>(yslot + (static_cast<int64_t>(t) * k + j) * H + h0);
+  u32x4 rows[KMAX];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] += X::to_f32(X::get(s, c));
+  for (int j = 0; j < KMAX; ++j)
+    rows[j] = *reinterpret_cast<const u32x4*>(yslot + (static_cast<int64_t>(t) * k + min(j, k - 1)) * H + h0);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) acc[c] += X::to_f32(X::get(rows[j], c));
+    }
   }
   u32x4 o;
   if constexpr (X::ES == 2) {
@@ -584,7 +593,9 @@ template <typename T>
 hipError_t launch_combine(const T* yslot, int T_, int k, int H, T* y, hipStream_t st) {
   constexpr int VEC = Elt<T>::VEC;
   const dim3 grid(T_, (H + 256 * VEC - 1) / (256 * VEC));
-  hipLaunchKernelGGL(k_combine<T>, grid, dim3(256), 0, st, yslot, k, H, y);
+  if (k <= 2) hipLaunchKernelGGL((k_combine<T, 2>), grid, dim3(256), 0, st, yslot, k, H, y);
+  else if (k <= 8) hipLaunchKernelGGL((k_combine<T, 8>), grid, dim3(256), 0, st, yslot, k, H, y);
+  else hipLaunchKernelGGL((k_combine<T, kMaxK>), grid, dim3(256), 0, st, yslot, k, H, y);
   return hipGetLastError();
 }
 template hipError_t launch_combine<uint16_t>(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
