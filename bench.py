@@ -323,6 +323,41 @@ def copy_foil_bench(args, cfg, x, lgd, pool, ptd, pt, bufs, dev, R, torch, np):
             "ms_per_step_gather_then_layer": round(step_ms, 4), "bitwise_equal_output": same}
 
 
+def graph_bench(args, cfg, x, lgd, pool, ptd, bufs, R, torch):
+    """The same layer captured once in a HIP graph and replayed: one graph
+    launch per step instead of the host enqueueing each kernel."""
+    def layer():
+        R.fused_moe_paged(x, lgd, pool, ptd, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
+    layer()
+    torch.cuda.synchronize()
+    y_eager = bufs.y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(bufs.y, y_eager))
+    e0, e1 = R.event_create(), R.event_create()
+    R.event_record(e0)
+    for _ in range(args.steps):
+        g.replay()
+    R.event_record(e1)
+    torch.cuda.synchronize()
+    ms = R.event_elapsed_ms(e0, e1) / args.steps
+    R.event_destroy(e0)
+    R.event_destroy(e1)
+    del g
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(x.shape[0] / (ms * 1e-3), 1),
+            "bitwise_equal_output": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +375,7 @@ def main():
                     help="skip the host-side adjuster policy measurement")
     ap.add_argument("--attn-requests", type=int, default=256,
                     help="decode-attention requests taken from the layout's KV view (0: skip)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the layer")
     ap.add_argument("--no-foil", action="store_true",
                     help="skip the gather-then-contiguous foil (the copy the paged kernel avoids)")
     ap.add_argument("--no-router", action="store_true",
@@ -507,6 +543,11 @@ def main():
     if args.upload_experts:
         upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
+    # Timed region 8: the layer captured in a HIP graph, replayed.
+    graph = None
+    if not args.no_graph and args.flush_mib == 0:
+        graph = graph_bench(args, cfg, x, lgd, pool, ptd, bufs, R, torch)
+
     # Timed region 7: the foil -- gather the touched experts, then the layer.
     foil = None
     if not args.no_foil:
@@ -600,6 +641,9 @@ def main():
         out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
     if attn is not None:
         out["attention"] = attn
+    if graph is not None:
+        graph["over_eager"] = round(graph["ms_per_step"] / ms_step, 4)
+        out["graph_replay"] = graph
     if foil is not None:
         foil["foil_over_paged"] = round(foil["ms_per_step_gather_then_layer"] / ms_step, 3)
         out["copy_foil"] = foil
