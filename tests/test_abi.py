@@ -191,3 +191,15 @@ def test_bench_is_one_gpu_only():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_layer_and_attention_never_copy_or_clear_memory():
+    """The paged kernel reads expert pages where they sit: no translation unit
+    of the layer or of the attention copies or clears device memory (the
+    only copy in the library is the expert upload from host memory)."""
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "paged_moe_expert_amd", "csrc")
+    for f in ("moe_layer.hip", "moe_routing.hip", "moe_gemm_stream.hip", "moe_gemm_tiled.hip", "attention.hip"):
+        src = open(os.path.join(csrc, f)).read()
+        for call in ("hipMemcpy", "hipMemset", "hipMalloc", "hipFree", "hipStreamSynchronize",
+                     "hipDeviceSynchronize"):
+            assert call not in src, f"{f} calls {call}"
