@@ -89,6 +89,10 @@ CUSTOM = [
     ("bf16-pipelined-tiles", 8, 2, 512, 256, 1200, "bf16", 4 * KIB, None),
     ("bf16-pipelined-odd-page-skewed", 8, 2, 512, 512, 1500, "bf16", 12 * KIB, [3, 2, 1, 0, 0, 0, -1, -40]),
     ("bf16-pipelined-many-experts", 32, 4, 512, 256, 1400, "bf16", 64 * KIB, None),
+    # the shape limits: 512 experts, top-32 (8 logits a lane in gating, a
+    # 32-row combine), with a wavefront per token and with one-workgroup routing
+    ("bf16-max-experts-and-k", 512, 32, 128, 64, 50, "bf16", 4 * KIB, None),
+    ("bf16-max-experts-and-k-8-tokens", 512, 32, 128, 64, 8, "bf16", 4 * KIB, None),
 ]
 
 
