@@ -116,9 +116,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_paged_attn(const uint16_t* __re
   const int blk0 = split * chunk, blk1 = min(blk0 + chunk, nblk);
   if (blk0 >= blk1) {             // nothing of this request in this split
     if (out != nullptr) {         // one split: an empty context gives zeros
-      const int G0 = n_q / n_kv;
-      uint16_t* o = out + (static_cast<int64_t>(b) * n_q + j * G0) * D;
-      for (int i = threadIdx.x; i < G0 * D; i += kWaves * 64) o[i] = 0;
+      uint16_t* o = out + (static_cast<int64_t>(b) * n_q + j * G) * D;
+      for (int i = threadIdx.x; i < G * D; i += kWaves * 64) o[i] = 0;
     }
     return;
   }

@@ -390,26 +390,6 @@ constexpr int kTinyThreads = 1024;
 constexpr int kTinyMaxT = 16;       // tokens
 constexpr int kTinyMaxTK = 512;     // routed slots
 
-__device__ __forceinline__ int block_excl_scan_1024(int v, int* total, int* sh) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) sh[wv] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < kTinyThreads / 64; ++i) {
-    before += (i < wv) ? sh[i] : 0;
-    all += sh[i];
-  }
-  *total = all;
-  return before + incl - v;
-}
-
 template <int EPL>
 __global__ __launch_bounds__(kTinyThreads) void k_route_tiny(const float* __restrict__ logits, int T, int E, int k,
                                                              int BM, int32_t* __restrict__ topk_ids,
@@ -450,7 +430,7 @@ __global__ __launch_bounds__(kTinyThreads) void k_route_tiny(const float* __rest
   const int cnt = e < E ? hist[e] : 0;
   const int padded = (cnt + BM - 1) / BM * BM;
   int total;
-  const int seg = block_excl_scan_1024(padded, &total, sh);
+  const int seg = block_excl_scan<kTinyThreads>(padded, &total, sh);
   if (e < E) {
     hist[e] = seg;                                  // segment starts (counts are no longer needed)
     expert_off[e] = seg;
