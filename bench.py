@@ -358,6 +358,30 @@ def graph_bench(args, cfg, x, lgd, pool, ptd, bufs, R, torch):
             "bitwise_equal_output": same}
 
 
+def read_ceiling(args, dev, R, torch):
+    """A plain streaming read on this GPU (rimuru_stream_read: one pass of
+    16-byte loads over a 4 GiB buffer), event-timed; the practical bound
+    beside the datasheet peak."""
+    n = (4096 << 20) // 4
+    buf = torch.ones(n, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        R.stream_read(buf, sink)
+    e0, e1 = R.event_create(), R.event_create()
+    torch.cuda.synchronize()
+    R.event_record(e0)
+    reps = 5
+    for _ in range(reps):
+        R.stream_read(buf, sink)
+    R.event_record(e1)
+    torch.cuda.synchronize()
+    ms = R.event_elapsed_ms(e0, e1) / reps
+    R.event_destroy(e0)
+    R.event_destroy(e1)
+    del buf
+    return 4 * n / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,6 +567,9 @@ def main():
     if args.upload_experts:
         upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
+    # Timed region 9: the measured streaming-read ceiling.
+    ceiling = read_ceiling(args, dev, R, torch)
+
     # Timed region 8: the layer captured in a HIP graph, replayed.
     graph = None
     if not args.no_graph and args.flush_mib == 0:
@@ -641,6 +668,10 @@ def main():
         out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
     if attn is not None:
         out["attention"] = attn
+    out["measured_read_ceiling"] = {"gbs": round(ceiling, 1), "method": "rimuru_stream_read over a 4 GiB buffer",
+                                    "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4)}
+    if roof["bound"] == "hbm":
+        out["measured_read_ceiling"]["dominant_kernel_frac_of_it"] = round(roof["achieved"] / ceiling, 4)
     if graph is not None:
         graph["over_eager"] = round(graph["ms_per_step"] / ms_step, 4)
         out["graph_replay"] = graph

@@ -443,6 +443,16 @@ rimuru_status rimuru_event_destroy(void* ev);
 rimuru_status rimuru_event_record(void* ev, void* hip_stream);
 rimuru_status rimuru_event_elapsed_ms(void* start, void* stop, float* ms);
 
+/* Calibration read: enqueue one plain streaming read of buf (every 16-byte
+ * piece loaded once, non-temporally, by a grid-stride loop with eight loads
+ * in flight per thread), the practical read bound of the GPU beside its
+ * datasheet peak.
+ * Nothing is written except, if the XOR of all the data equals 0x5A5A5A5A,
+ * that value to *sink (a device uint32; the store keeps the loads live).
+ *   buf: device, 16-byte aligned; bytes: a multiple of 16.
+ * Errors: EINVAL, EHIP. */
+rimuru_status rimuru_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,6 +102,7 @@ _PROTOS = {
     "rimuru_event_destroy": (C.c_int32, [C.c_void_p]),
     "rimuru_event_record": (C.c_int32, [C.c_void_p, C.c_void_p]),
     "rimuru_event_elapsed_ms": (C.c_int32, [C.c_void_p, C.c_void_p, C.POINTER(C.c_float)]),
+    "rimuru_stream_read": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
 }
 
 _lib = None

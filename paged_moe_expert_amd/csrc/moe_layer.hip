@@ -249,6 +249,15 @@ extern "C" rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt
   return RIMURU_OK;
 }
 
+extern "C" rimuru_status rimuru_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* hip_stream) {
+  if (buf == nullptr || sink == nullptr) return rimuru_fail(RIMURU_EINVAL, "stream_read: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || bytes % 16 != 0)
+    return rimuru_fail(RIMURU_EINVAL, "stream_read: buf must be 16-byte aligned and bytes a multiple of 16");
+  const hipError_t err = launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "stream_read: launch failed: %s", hipGetErrorString(err));
+  return RIMURU_OK;
+}
+
 extern "C" rimuru_status rimuru_event_create(void** ev) {
   if (!ev) return rimuru_fail(RIMURU_EINVAL, "event_create: NULL");
   hipEvent_t e;

@@ -508,6 +508,42 @@ __global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool,
   }
 }
 
+// ---------------------------------------------------------------- calibration read
+
+// One pass over buf: each thread loads 16-byte pieces gtid, gtid + stride,
+// ... eight at a time (independent non-temporal loads in flight; measured the
+// fastest of plain/non-temporal loads, 4/8/16 in flight and grids of 1024 to
+// 16384 workgroups), XOR-folds them, and stores only when the fold equals a
+// fixed pattern, so no load can be dropped and (almost) nothing is written.
+constexpr int kReadUnroll = 8;
+constexpr int kReadGrid = 16384;
+
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ buf, uint64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = buf[i];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  if (acc == 0x5A5A5A5Au) *sink = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t st) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stream_read, dim3(kReadGrid), dim3(256), 0, st, static_cast<const u32x4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 PageDiv make_div(uint32_t page) {

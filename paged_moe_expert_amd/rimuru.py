@@ -360,6 +360,15 @@ def event_destroy(ev: int) -> None:
     check(lib().rimuru_event_destroy(ev), "event_destroy")
 
 
+def stream_read(buf, sink, stream=None) -> None:
+    """Enqueue one plain streaming read of the device tensor buf (calibration);
+    sink is a device int32/uint32 tensor of at least one element."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    check(lib().rimuru_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                   s.cuda_stream), "stream_read")
+
+
 def event_record(ev: int, stream=None) -> None:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()

@@ -203,3 +203,11 @@ def test_layer_and_attention_never_copy_or_clear_memory():
         for call in ("hipMemcpy", "hipMemset", "hipMalloc", "hipFree", "hipStreamSynchronize",
                      "hipDeviceSynchronize"):
             assert call not in src, f"{f} calls {call}"
+
+
+def test_stream_read_rejects_bad_arguments_without_launching():
+    lib = _lib.lib()
+    assert lib.rimuru_stream_read(None, 1024, 1 << 20, None) == _lib.EINVAL
+    assert lib.rimuru_stream_read(1 << 20, 1024, None, None) == _lib.EINVAL
+    assert lib.rimuru_stream_read((1 << 20) + 8, 1024, 1 << 21, None) == _lib.EINVAL
+    assert lib.rimuru_stream_read(1 << 20, 1000, 1 << 21, None) == _lib.EINVAL
