@@ -1,10 +1,16 @@
 """Benchmark of the paged fused-MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--nested 2,3] [--no-cpu]
 
-Workload (default): the Qwen3-30B-A3B-shaped decode layer -- 64 tokens,
-128 experts, top-8, hidden 2048, inter 768, bf16 weights on one 3 MiB page per
-projection at seeded positions of a 4 GiB pool interleaved with KV blocks.
+Headline workload (default): the large prefill with sub-page fragmentation --
+8192 tokens, 128 experts, top-8, hidden 2048, inter 768, bf16 weights split
+into 64 KiB pages placed by 10,000 seeded allocator events on a 4 GiB pool
+shared with KV blocks, Zipf(1.2) routing. It is the largest single-GPU
+configuration and the MFMA-bound one. The Qwen3-30B-A3B-shaped decode layer
+(64 tokens, one 3 MiB page per projection) and the Qwen3.5-35B-A3B-shaped
+prefill (2048 tokens, 256 experts) are measured in the same run and nested in
+the line under "other_workloads", each with its own roofline.
+
 Inputs are synthetic and resident in HBM before timing starts. One step is
 one call of the whole layer (gating, count, sort, gate/up GEMM, down GEMM,
 combine). Prints one JSON line.
@@ -54,8 +60,23 @@ def traffic_from_profiles(workload: str, kernel: str, kind: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, xb, lg, wb, n_tokens: int):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    routing of every token, the page resolution of every expert the sample
+    touches, and the fp64 expert MLPs and combine of the sampled tokens. The
+    BLAS thread count is the process's own (OMP_NUM_THREADS where the host
+    sets it for this job's CPU share); cores reports the threads the BLAS
+    pools actually ran with."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -70,9 +91,15 @@ def cpu_baseline(cfg, xb, lg, wb, n_tokens: int):
                 dtype=cfg.dtype, tokens=toks)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_tokens} of {cfg.T} tokens (routing over all {cfg.T}), fp64 numpy, "
-                      f"page resolution included; {dt:.2f} s"}
+            "sample": f"the first {n_tokens} of {cfg.T} tokens (routing over all {cfg.T}, pages of every "
+                      f"expert they touch resolved), fp64 numpy; {dt:.2f} s",
+            "host_cpu_count": os.cpu_count(), "host_affinity_cpus": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"), "cpu_model": cpu_model()}
 
 
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
@@ -382,58 +409,10 @@ def read_ceiling(args, dev, R, torch):
     return 4 * n / (ms * 1e-3) / 1e9
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--tokens", type=int, default=0, help="override T (decode sweep)")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
-    ap.add_argument("--copy-calibration", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--upload-experts", type=int, default=8,
-                    help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
-    ap.add_argument("--no-adjuster", action="store_true",
-                    help="skip the host-side adjuster policy measurement")
-    ap.add_argument("--attn-requests", type=int, default=256,
-                    help="decode-attention requests taken from the layout's KV view (0: skip)")
-    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the layer")
-    ap.add_argument("--no-foil", action="store_true",
-                    help="skip the gather-then-contiguous foil (the copy the paged kernel avoids)")
-    ap.add_argument("--no-router", action="store_true",
-                    help="skip the run that computes the router projection in the gating stage")
-    ap.add_argument("--no-contiguous", action="store_true",
-                    help="skip the comparison run on a contiguous layout of the same weights")
-    ap.add_argument("--flush-mib", type=int, default=0,
-                    help="before every timed step, read this many MiB of scratch (evicts the "
-                         "Infinity Cache with clean lines); steps are then timed by an event pair each")
-    args = ap.parse_args()
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the paged fused-MoE layer runs on a single "
-              "MI355X here and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from moe_inputs import CONFIGS, gen
-    from paged_moe_expert_amd import rimuru as R
+def setup_layer(cfg, T, dev, R, torch, np, gen):
+    """Layout, weights on their pages and device-resident inputs (untimed)."""
     from paged_moe_expert_amd.layouts import DeviceLayout
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    cfg = CONFIGS[args.config]
-    T = args.tokens or cfg.T
-    dev = torch.device("cuda:0")
-    log(f"[bench] {cfg.name}: T={T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} {cfg.dtype} "
-        f"page={cfg.page_bytes} pool={cfg.pool_bytes >> 20} MiB")
-
-    # ---- layout and device-resident inputs (untimed)
     t0 = time.perf_counter()
     lay = DeviceLayout(cfg).run()
     pt = lay.page_table()
@@ -452,7 +431,19 @@ def main():
     dt_code = R.BF16 if cfg.dtype == "bf16" else R.F32
     bufs = R.MoeBuffers(T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.P, dt_code, device=dev)
     torch.cuda.synchronize()
-    log(f"[bench] setup {time.perf_counter() - t0:.1f} s")
+    log(f"[bench] {cfg.name}: setup {time.perf_counter() - t0:.1f} s")
+    return dict(lay=lay, pt=pt, wb=wb, xb=xb, lg=lg, tdt=tdt, idt=idt, pool=pool, ptd=ptd, x=x, lgd=lgd,
+                bufs=bufs)
+
+
+def measure(args, cfg, T, extras, dev, R, torch, np, gen):
+    """Time the layer on one configuration; returns the result object (the
+    headline fields plus the extras asked for)."""
+    log(f"[bench] {cfg.name}: T={T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} {cfg.dtype} "
+        f"page={cfg.page_bytes} pool={cfg.pool_bytes >> 20} MiB")
+    L = setup_layer(cfg, T, dev, R, torch, np, gen)
+    lay, pt, wb, idt, tdt = L["lay"], L["pt"], L["wb"], L["idt"], L["tdt"]
+    pool, ptd, x, lgd, bufs = L["pool"], L["ptd"], L["x"], L["lgd"], L["bufs"]
 
     def step(events=None):
         R.fused_moe_paged(x, lgd, pool, ptd, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs,
@@ -461,7 +452,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("[bench] warmup done")
+    log(f"[bench] {cfg.name}: warmup done")
 
     # Timed region 1: the headline. Stage events are left out here because
     # each event record costs the stream a few microseconds.
@@ -512,13 +503,13 @@ def main():
     for row in evs:
         for e in row:
             R.event_destroy(e)
-    log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms "
+    log(f"[bench] {cfg.name}: timed {args.steps} steps in {wall * 1e3:.2f} ms "
         f"({wall_events * 1e3:.2f} ms with stage events)")
 
     # Timed region 3: the same layer on a contiguous layout of the same weights
     # (pages consecutive and in order), for the cost of paging.
     cont = None
-    if not args.no_contiguous:
+    if "contiguous" in extras:
         from paged_moe_expert_amd.layouts import contiguous_page_table
         cpt = torch.from_numpy(contiguous_page_table(cfg)).to(dev)
         cpool = torch.empty(cfg.E * 3 * cfg.P * cfg.page_bytes, dtype=torch.uint8, device=dev)
@@ -529,6 +520,7 @@ def main():
         R.fused_moe_paged(x, lgd, cpool, cpt, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
         torch.cuda.synchronize()
         same = bool(torch.equal(ybuf.view(torch.uint8), bufs.y.view(torch.uint8)))
+
         def cstep():
             R.fused_moe_paged(x, lgd, cpool, cpt, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
         for _ in range(args.warmup):
@@ -537,10 +529,10 @@ def main():
         del cpool
         cont = {"ms_per_step": round(cont_ms, 4), "bitwise_equal_output": same}
 
-    # Timed region 5: the same layer computing its router logits x . w_gate^T
+    # Timed region 4: the same layer computing its router logits x . w_gate^T
     # in the gating stage (w_gate [E, H] instead of given logits).
     router = None
-    if not args.no_router:
+    if "router" in extras:
         wg = torch.from_numpy(gen.gate_weight_bits(cfg).view(idt)).to(dev).view(tdt)
 
         def rstep(events=None):
@@ -561,40 +553,27 @@ def main():
                   "gating_with_router_us_median": round(float(np.median(gate_ms)) * 1e3, 2),
                   "router_gflop": round(2.0 * T * cfg.E * cfg.H / 1e9, 4)}
 
-    # Timed region 4: dual-buffer expert upload (host -> fresh expert pages on a
+    # Timed region 5: dual-buffer expert upload (host -> fresh expert pages on a
     # copy stream), alone and overlapped with the layer on the compute stream.
     upload = None
-    if args.upload_experts:
+    if "upload" in extras and args.upload_experts:
         upload = expert_upload_bench(args, cfg, wb, idt, dev, step, R, torch, np)
 
-    # Timed region 9: the measured streaming-read ceiling.
-    ceiling = read_ceiling(args, dev, R, torch)
-
-    # Timed region 8: the layer captured in a HIP graph, replayed.
+    # Timed region 6: the layer captured in a HIP graph, replayed.
     graph = None
-    if not args.no_graph and args.flush_mib == 0:
+    if "graph" in extras and args.flush_mib == 0:
         graph = graph_bench(args, cfg, x, lgd, pool, ptd, bufs, R, torch)
 
     # Timed region 7: the foil -- gather the touched experts, then the layer.
     foil = None
-    if not args.no_foil:
+    if "foil" in extras:
         foil = copy_foil_bench(args, cfg, x, lgd, pool, ptd, pt, bufs, dev, R, torch, np)
 
-    # Timed region 6: paged decode attention over the same pool's KV view.
+    # Timed region 8: paged decode attention over the same pool's KV view.
     attn = None
-    if args.attn_requests and cfg.dtype == "bf16" and any(v.name == "kv" for v in cfg.views) \
-            and any(name == "kv" for name, _ in lay.live):
+    if "attention" in extras and args.attn_requests and cfg.dtype == "bf16" \
+            and any(v.name == "kv" for v in cfg.views) and any(name == "kv" for name, _ in lay.live):
         attn = attention_bench(args, cfg, lay, pool, dev, R, torch, np)
-
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {n} bytes done")
 
     # ---- algorithmic work of this input
     off = bufs.expert_off.cpu().numpy()
@@ -609,6 +588,8 @@ def main():
     flops = 6.0 * HI * TK
     up_bytes = touched * 2 * HI * es + T * cfg.H * es + TK * cfg.I * es
     up_flops = 4.0 * HI * TK
+    dn_bytes = touched * HI * es + TK * cfg.I * es + TK * cfg.H * es
+    dn_flops = 2.0 * HI * TK
 
     ms_step = wall * 1e3 / args.steps
     if step_ms is not None:
@@ -618,75 +599,192 @@ def main():
         step_src = "sum of the stage-event intervals of each step (event records included)"
     med = np.median(stage_ms, axis=0)
     mean = stage_ms.mean(axis=0)
-    up_ms = float(mean[3])
     decode_like = (w_bytes + io_bytes) / HBM_PEAK_GBS > flops / (BF16_PEAK_TFLOPS * 1e3)
     kind = "stream" if bufs.block_m == 16 else "tiled"
-    if decode_like:
-        achieved = up_bytes / (up_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "gemm_up", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(cfg.name, "gemm_up", kind),
-                "algorithmic_bytes_per_launch": up_bytes, "avg_launch_us": round(up_ms * 1e3, 2)}
-    else:
-        achieved = up_flops / (up_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_up", "achieved": round(achieved, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles(cfg.name, "gemm_up", kind),
-                "algorithmic_flops_per_launch": up_flops, "avg_launch_us": round(up_ms * 1e3, 2)}
 
+    def kernel_roof(name, ms, nbytes, nflops, traffic):
+        if decode_like:
+            a = nbytes / (ms * 1e-3) / 1e9
+            return {"bound": "hbm", "kernel": name, "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
+        a = nflops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": name, "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": nflops, "algorithmic_bytes_per_launch": nbytes,
+                "avg_launch_us": round(ms * 1e3, 2)}
+
+    roof = kernel_roof("gemm_up", float(mean[3]), up_bytes, up_flops,
+                       traffic_from_profiles(cfg.name, "gemm_up", kind))
+    roof_dn = kernel_roof("gemm_down", float(mean[4]), dn_bytes, dn_flops,
+                          traffic_from_profiles(cfg.name, "gemm_down", kind))
+    layer_roof_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), (w_bytes + io_bytes) / (HBM_PEAK_GBS * 1e9)) * 1e6
     out = {
-        "metric": "paged fused-MoE tokens/s + TFLOP/s (or HBM GB/s) as % of MI355X roofline",
         "value": round(T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I,
-                   "page_bytes": cfg.page_bytes, "pool_bytes": cfg.pool_bytes,
+                   "page_bytes": cfg.page_bytes, "pages_per_projection": cfg.P, "pool_bytes": cfg.pool_bytes,
                    "experts_touched": touched, "block_m": bufs.block_m,
+                   "routed_rows_max_min": [int(counts.max()), int(counts.min())],
                    "cache_flush_mib": args.flush_mib},
         "layer": {"tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "hbm_gbs": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9, 1),
+                  "hbm_frac": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "algorithmic_bytes": w_bytes + io_bytes, "algorithmic_flops": flops,
-                  "hbm_frac": round((w_bytes + io_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                  "bound": "hbm" if decode_like else "mfma",
+                  "roofline_us": round(layer_roof_us, 2),
+                  "roofline_frac": round(layer_roof_us / (ms_step * 1e3), 4)},
         "stages_us_median": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, med)},
+        "stages_us_mean": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, mean)},
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "step_ms_source": step_src,
         "ms_per_step_with_stage_events": round(wall_events * 1e3 / args.steps, 4),
         "roofline": roof,
+        "roofline_gemm_down": roof_dn,
     }
+    if cont is not None:
+        cont["paged_over_contiguous_minus_1"] = round(ms_step / cont["ms_per_step"] - 1.0, 4)
+        out["contiguous"] = cont
+    if router is not None:
+        router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
+        out["with_router"] = router
     if upload is not None:
         out["expert_upload"] = upload
-    if not args.no_adjuster and any(v.name == "kv" and v.parent == "expert" for v in cfg.views):
+    if "adjuster" in extras and any(v.name == "kv" and v.parent == "expert" for v in cfg.views):
         gbs = upload["upload_gbs_alone"] if upload is not None else None
         out["adjuster"] = adjuster_bench(cfg, R, np, gen, gbs)
     if attn is not None:
         out["attention"] = attn
-    out["measured_read_ceiling"] = {"gbs": round(ceiling, 1), "method": "rimuru_stream_read over a 4 GiB buffer",
-                                    "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4)}
-    if roof["bound"] == "hbm":
-        out["measured_read_ceiling"]["dominant_kernel_frac_of_it"] = round(roof["achieved"] / ceiling, 4)
     if graph is not None:
         graph["over_eager"] = round(graph["ms_per_step"] / ms_step, 4)
         out["graph_replay"] = graph
     if foil is not None:
         foil["foil_over_paged"] = round(foil["ms_per_step_gather_then_layer"] / ms_step, 3)
         out["copy_foil"] = foil
-    if router is not None:
-        router["added_ms_vs_given_logits"] = round(router["ms_per_step"] - ms_step, 4)
-        out["with_router"] = router
-    if cont is not None:
-        cont["paged_over_contiguous_minus_1"] = round(ms_step / cont["ms_per_step"] - 1.0, 4)
-        out["contiguous"] = cont
-    if not args.no_cpu:
-        log("[bench] timing the oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(cfg.with_T(T), xb, lg, wb, min(args.cpu_tokens, T))
+    if "cpu" in extras:
+        log(f"[bench] {cfg.name}: timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(cfg.with_T(T), L["xb"], L["lg"], wb, min(args.cpu_tokens, T))
+    del L, pool, bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+EXTRAS_ALL = ("contiguous", "router", "upload", "graph", "foil", "attention", "adjuster")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, help="headline configuration (default: the 8192-token "
+                                                           "fragmented prefill)")
+    ap.add_argument("--nested", default="2,3",
+                    help="other configurations measured in the same run, nested in the line ('' = none)")
+    ap.add_argument("--tokens", type=int, default=0, help="override T of the headline (decode sweep)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--upload-experts", type=int, default=8,
+                    help="experts uploaded host -> fresh pages for the expert-upload measurement (0 = skip)")
+    ap.add_argument("--no-adjuster", action="store_true",
+                    help="skip the host-side adjuster policy measurement")
+    ap.add_argument("--attn-requests", type=int, default=256,
+                    help="decode-attention requests taken from the layout's KV view (0: skip)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the layer")
+    ap.add_argument("--no-foil", action="store_true",
+                    help="skip the gather-then-contiguous foil (the copy the paged kernel avoids)")
+    ap.add_argument("--no-router", action="store_true",
+                    help="skip the run that computes the router projection in the gating stage")
+    ap.add_argument("--no-contiguous", action="store_true",
+                    help="skip the comparison run on a contiguous layout of the same weights")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="before every timed step, read this many MiB of scratch (evicts the "
+                         "Infinity Cache with clean lines); steps are then timed by an event pair each")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the paged fused-MoE layer runs on a single "
+              "MI355X here and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_inputs import CONFIGS, gen
+    from paged_moe_expert_amd import rimuru as R
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    skip = {"contiguous": args.no_contiguous, "router": args.no_router, "graph": args.no_graph,
+            "foil": args.no_foil, "adjuster": args.no_adjuster, "upload": args.upload_experts == 0,
+            "attention": args.attn_requests == 0}
+    extras = {e for e in EXTRAS_ALL if not skip.get(e, False)}
+
+    cfg = CONFIGS[args.config]
+    T = args.tokens or cfg.T
+    head = measure(args, cfg, T, extras | ({"cpu"} if not args.no_cpu else set()), dev, R, torch, np, gen)
+
+    nested = {}
+    for tok in filter(None, (t.strip() for t in args.nested.split(","))):
+        cid = int(tok)
+        if cid == args.config:
+            continue
+        c2 = CONFIGS[cid]
+        # the decode layer carries the serving-side measurements (upload,
+        # adjuster, attention, graph); the prefill layers the paging ones
+        sub = {"contiguous", "router", "foil"} & extras
+        if c2.T * c2.k <= 24 * c2.E:
+            sub = set(extras)
+        nested[c2.name] = measure(args, c2, c2.T, sub, dev, R, torch, np, gen)
+
+    # the measured streaming-read ceiling
+    ceiling = None if args.no_ceiling else read_ceiling(args, dev, R, torch)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+
+    out = {
+        "metric": "paged fused-MoE tokens/s + TFLOP/s (or HBM GB/s) as % of MI355X roofline",
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": head.pop("config"),
+        "roofline": head.pop("roofline"),
+    }
+    cpu = head.pop("cpu_baseline", None)
+    out.update(head)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    if ceiling is not None:
+        out["measured_read_ceiling"] = {"gbs": round(ceiling, 1),
+                                        "method": "rimuru_stream_read over a 4 GiB buffer",
+                                        "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4)}
+    if nested:
+        out["other_workloads"] = nested
     print(json.dumps(out), flush=True)
 
 

@@ -176,9 +176,9 @@ rimuru_status rimuru_pool_check(const rimuru_pool* pool);
 /* The policy that moves the fence between the expert view and the KV view
  * (paper summary: abstract, "workload-aware adjuster", and Figure 8;
  * explainer "Rimuru unifies serving memory", paragraph on the two pieces that
- * make the moving fence usable: grow the KV side when concurrency climbs,
- * give space back to the experts when requests finish, and keep expert loads
- * and evictions from colliding with the prefetch pipeline). The pages give no
+ * make the moving fence usable: rising request counts shift budget toward the
+ * KV view, KV blocks freed by finished requests shift it back, and the
+ * prefetch path's uploads are never evicted mid-flight). The pages give no
  * rule beyond that; the rule below is this library's reading.
  *
  * Experts are expert-view owners 3e + p (p = 0, 1, 2 for w1, w3, w2), P pages
@@ -272,8 +272,9 @@ rimuru_status rimuru_adjuster_state(const rimuru_adjuster* adj, uint8_t* residen
  *   out[b, h] = softmax_t(scale * q[b, h] . K_b[t]) V_b, t < context_lens[b],
  * accumulated in fp32 (probabilities rounded to bf16 for the second
  * product), written as bf16; context length 0 gives zeros. Token slots past
- * the context in a request's last block get probability 0 but are still
- * multiplied, so they must hold finite values (0 * NaN is NaN). */
+ * the context in a request's last block may hold any bytes (NaN and Inf
+ * included: blocks are cut from pages that held other tensors): their scores
+ * and their V values are selected away, never multiplied in. */
 typedef struct {
   int32_t B;               /* requests (one query token each), >= 0 */
   int32_t n_q;             /* query heads: a multiple of n_kv, <= 16 * n_kv */
@@ -402,13 +403,18 @@ rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int32_t P,
                               uint64_t page_bytes, uint64_t pool_bytes);
 
 /* Load expert weights into their pages: copy src (device, [E][3][proj_bytes]
- * contiguous) into the pool pages pt names, page by page, on hip_stream.
- * This is how weights reach the pool (the reverse of the contiguous copy the
- * layer avoids); it is not part of the layer. proj_bytes <= P*page_bytes,
- * proj_bytes a multiple of 16, page_bytes a multiple of 128.
+ * contiguous) into the pool pages pt (device [E][3][P]) names, page by page,
+ * on hip_stream. This is how weights reach the pool (the reverse of the
+ * contiguous copy the layer avoids); it is not part of the layer.
+ * pool_bytes is the pool's size: a pt entry naming a page outside
+ * [0, pool_bytes) is skipped on the device (that page's bytes are not
+ * stored; nothing outside the pool is written). pt lives on the device and
+ * is not read on the host here: check a host copy with rimuru_pt_check first
+ * to have such entries reported (the Python binding does). proj_bytes <=
+ * P*page_bytes, proj_bytes a multiple of 16, page_bytes a multiple of 128.
  * Errors: EINVAL, EHIP. */
-rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt, int32_t E, int32_t P,
-                                   uint64_t page_bytes, const void* src, uint64_t proj_bytes,
+rimuru_status rimuru_experts_store(void* pool_base, uint64_t pool_bytes, const int32_t* pt, int32_t E,
+                                   int32_t P, uint64_t page_bytes, const void* src, uint64_t proj_bytes,
                                    void* hip_stream);
 
 /* Elastic expert offloading, dual-buffer upload (Rimuru paper summary,

@@ -3,12 +3,12 @@
 Written from the Rimuru pages: the paper summary's abstract (a workload-aware
 adjuster reallocates pages across tensor types by runtime demand), its
 Figure 8 (expert prefetch overlapped with execution) and the explainer's
-paragraph on the two pieces that make the moving fence usable (the adjuster
-grows the KV side when concurrency climbs, gives space back to the experts
-when requests finish and free their KV pages, and works with the prefetch
-pipeline so that expert loads and evictions do not collide). The pages give
-no rule beyond that; this is the plain reading (the product's adjuster must
-take the same decisions):
+paragraph on the two pieces that make the moving fence usable. What those
+say, in this module's terms: more concurrent requests move budget from the
+expert view to the KV view; finished requests release KV blocks whose budget
+returns to the experts; and an expert being uploaded by the prefetch path is
+never chosen for eviction. The pages give no rule beyond that; this is the
+plain reading (the product's adjuster must take the same decisions):
 
 * State: which experts are resident (all three projections, P pages each, as
   expert-view owners 3e + p), which have an upload in flight (loaded, not

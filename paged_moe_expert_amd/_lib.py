@@ -89,8 +89,8 @@ _PROTOS = {
     "rimuru_fused_moe_paged": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p]),
     "rimuru_fused_moe_paged_router": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p, C.c_void_p, C.c_void_p]),
     "rimuru_pt_check": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_uint64, C.c_uint64]),
-    "rimuru_experts_store": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_uint64,
-                                         C.c_void_p, C.c_uint64, C.c_void_p]),
+    "rimuru_experts_store": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_int32, C.c_int32,
+                                         C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]),
     "rimuru_expert_upload": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_int32, C.c_uint64,
                                          C.c_void_p, C.c_uint64, C.c_void_p]),
     "rimuru_attn_sizes": (C.c_int32, [C.c_int32] * 5 + [C.POINTER(C.c_uint64), C.POINTER(C.c_int32),

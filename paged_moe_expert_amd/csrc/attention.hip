@@ -92,10 +92,18 @@ __device__ __forceinline__ void attend_block(SoftmaxState<D>& st, const AttnFrag
   st.m = mn;
   const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
   const v4i16 pv = __builtin_bit_cast(v4i16, pb);
+  // V values of tokens at or past the context end are selected to zero, not
+  // multiplied by p = 0: the tail of a request's last block holds whatever
+  // the page held before (pages move between tensor types), and a NaN there
+  // times zero would still be NaN. This lane's V values are tokens t0 .. t0+3,
+  // token r in bits 16(r%2) of word r/2.
+  const u32x2 vmask = {(t0 < L ? 0x0000ffffu : 0u) | (t0 + 1 < L ? 0xffff0000u : 0u),
+                       (t0 + 2 < L ? 0x0000ffffu : 0u) | (t0 + 3 < L ? 0xffff0000u : 0u)};
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     f32x4 o = st.o[c] * alpha;
-    st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, f.v[c]), pv, o, 0, 0, 0);
+    const u32x2 vv = f.v[c] & vmask;
+    st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vv), pv, o, 0, 0, 0);
   }
 }
 

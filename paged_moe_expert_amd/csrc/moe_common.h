@@ -241,7 +241,7 @@ template <typename T>
 hipError_t launch_combine(const T* yslot, int T_, int k, int H, T* y, hipStream_t st);
 
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t st);
-hipError_t launch_store_pages(uint8_t* pool, const int32_t* pt, int P, uint32_t page_bytes,
+hipError_t launch_store_pages(uint8_t* pool, uint64_t pool_bytes, const int32_t* pt, int P, uint32_t page_bytes,
                               const uint8_t* src, uint64_t proj_bytes, uint64_t n_segs, hipStream_t st);
 
 // Page-table entries a streaming workgroup stages in LDS (both gated matrices).

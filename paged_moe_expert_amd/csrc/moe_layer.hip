@@ -229,11 +229,14 @@ extern "C" rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int3
   return RIMURU_OK;
 }
 
-extern "C" rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt, int32_t E, int32_t P,
-                                              uint64_t page_bytes, const void* src,
+extern "C" rimuru_status rimuru_experts_store(void* pool_base, uint64_t pool_bytes, const int32_t* pt, int32_t E,
+                                              int32_t P, uint64_t page_bytes, const void* src,
                                               uint64_t proj_bytes, void* hip_stream) {
   if (!pool_base || !pt || !src || E < 1 || P < 1)
     return rimuru_fail(RIMURU_EINVAL, "experts_store: bad argument");
+  if (pool_bytes < page_bytes)
+    return rimuru_fail(RIMURU_EINVAL, "experts_store: a pool of %llu bytes holds no page of %llu bytes",
+                       (unsigned long long)pool_bytes, (unsigned long long)page_bytes);
   if (page_bytes == 0 || page_bytes % 128 != 0 || proj_bytes == 0 || proj_bytes % 16 != 0 ||
       proj_bytes > static_cast<uint64_t>(P) * page_bytes ||
       static_cast<uint64_t>(P) * page_bytes >= (1ull << 31))
@@ -242,7 +245,8 @@ extern "C" rimuru_status rimuru_experts_store(void* pool_base, const int32_t* pt
   if (!aligned(pool_base, 256) || !aligned(src, 16))
     return rimuru_fail(RIMURU_EINVAL, "experts_store: pool_base needs 256-byte, src 16-byte alignment");
   uint64_t n_segs = static_cast<uint64_t>(E) * 3 * proj_bytes / 16;
-  hipError_t err = launch_store_pages(static_cast<uint8_t*>(pool_base), pt, P, static_cast<uint32_t>(page_bytes),
+  hipError_t err = launch_store_pages(static_cast<uint8_t*>(pool_base), pool_bytes, pt, P,
+                                      static_cast<uint32_t>(page_bytes),
                                       static_cast<const uint8_t*>(src), proj_bytes, n_segs,
                                       static_cast<hipStream_t>(hip_stream));
   if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "experts_store: %s", hipGetErrorString(err));

@@ -497,7 +497,10 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ yslot, in
 
 // ---------------------------------------------------------------- weight loading
 
-__global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool,
+// A page-table entry naming a page outside the pool (negative, or ending past
+// pool_bytes) is skipped: its bytes are not stored and nothing outside the
+// pool is ever written.
+__global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool, uint64_t pool_pages,
                                                      const int32_t* __restrict__ pt, int P,
                                                      PageDiv pd, const uint8_t* __restrict__ src,
                                                      uint64_t proj_bytes, uint64_t n_segs) {
@@ -506,7 +509,9 @@ __global__ __launch_bounds__(256) void k_store_pages(uint8_t* __restrict__ pool,
     uint64_t proj = byte / proj_bytes;
     uint32_t off = static_cast<uint32_t>(byte - proj * proj_bytes);
     uint32_t q = page_index(off, pd);
-    uint8_t* dst = pool + static_cast<uint64_t>(pt[proj * P + q]) * pd.page + (off - q * pd.page);
+    const int32_t pg = pt[proj * P + q];
+    if (pg < 0 || static_cast<uint64_t>(pg) >= pool_pages) continue;
+    uint8_t* dst = pool + static_cast<uint64_t>(pg) * pd.page + (off - q * pd.page);
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + byte);
   }
 }
@@ -620,12 +625,12 @@ hipError_t launch_combine(const T* yslot, int T_, int k, int H, T* y, hipStream_
 template hipError_t launch_combine<uint16_t>(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
 template hipError_t launch_combine<float>(const float*, int, int, int, float*, hipStream_t);
 
-hipError_t launch_store_pages(uint8_t* pool, const int32_t* pt, int P, uint32_t page_bytes,
+hipError_t launch_store_pages(uint8_t* pool, uint64_t pool_bytes, const int32_t* pt, int P, uint32_t page_bytes,
                               const uint8_t* src, uint64_t proj_bytes, uint64_t n_segs, hipStream_t st) {
   uint64_t blocks = (n_segs + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_store_pages, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, pool, pt, P,
-                     make_div(page_bytes), src, proj_bytes, n_segs);
+  hipLaunchKernelGGL(k_store_pages, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, pool,
+                     pool_bytes / page_bytes, pt, P, make_div(page_bytes), src, proj_bytes, n_segs);
   return hipGetLastError();
 }
 

@@ -274,12 +274,15 @@ def fused_moe_paged_raw(args: MoeArgs, stream_handle: int) -> int:
 
 def experts_store(pool, pt, weights, page_bytes: int, stream=None) -> None:
     """Copy contiguous projections weights [E, 3, proj_bytes] (device, uint8 view
-    or any dtype) into the pool pages pt names."""
+    or any dtype) into the pool pages pt names. A host copy of pt is checked
+    against the pool first (rimuru_pt_check: ERANGE for a page outside it)."""
     import torch
     E, three, P = pt.shape
     proj_bytes = weights[0, 0].numel() * weights.element_size()
+    pool_bytes = pool.numel() * pool.element_size()
+    pt_check(pt.cpu().numpy(), page_bytes, pool_bytes)
     s = stream if stream is not None else torch.cuda.current_stream(pool.device)
-    check(lib().rimuru_experts_store(pool.data_ptr(), pt.data_ptr(), E, P, page_bytes,
+    check(lib().rimuru_experts_store(pool.data_ptr(), pool_bytes, pt.data_ptr(), E, P, page_bytes,
                                      weights.data_ptr(), proj_bytes, s.cuda_stream), "experts_store")
 
 

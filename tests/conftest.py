@@ -26,3 +26,16 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    try:
+        from margins import RECORDS
+    except ImportError:  # pragma: no cover
+        return
+    if not RECORDS:
+        return
+    tr = terminalreporter
+    tr.section("parity margins (error / bound)")
+    for case, what, err, bound in RECORDS:
+        tr.write_line(f"{case:60s} {what:>14s} {err:10.3e} <= {bound:8.1e}  ({err / bound:6.3f} of the bound)")

@@ -14,6 +14,8 @@ from oracle.moe import moe_forward
 from paged_moe_expert_amd import rimuru as R
 from paged_moe_expert_amd.layouts import DeviceLayout
 
+from margins import record  # noqa: F401  (re-exported for the GPU tests)
+
 POISON = 0x7FC07FC0          # quiet NaN as fp32 and as two bf16
 
 
@@ -50,6 +52,25 @@ def paged_pool(pool_bytes: int, pt: np.ndarray, wdev: torch.Tensor, page_bytes: 
     ptd = torch.from_numpy(pt).cuda()
     R.experts_store(pool, ptd, wdev, page_bytes)
     return pool, ptd
+
+
+def host_pool(pool_bytes: int, page: int, pt: np.ndarray, wb: np.ndarray) -> np.ndarray:
+    """The oracle's pool, built on the host from the generator's weight bits
+    [E, 3, n] and a page table: zeros everywhere, page q of projection (e, p)
+    at pt[e, p, q] * page (the last page of a projection may be partial).
+    Nothing in it comes from the device."""
+    pool = np.zeros(pool_bytes, dtype=np.uint8)
+    raw = np.ascontiguousarray(wb).view(np.uint8).reshape(wb.shape[0], 3, -1)
+    nbytes = raw.shape[2]
+    for e in range(pt.shape[0]):
+        for p in range(3):
+            for q in range(pt.shape[2]):
+                lo, hi = q * page, min((q + 1) * page, nbytes)
+                if lo >= hi:
+                    break
+                a = int(pt[e, p, q]) * page
+                pool[a:a + hi - lo] = raw[e, p, lo:hi]
+    return pool
 
 
 def contiguous_pool(cfg, wdev: torch.Tensor):

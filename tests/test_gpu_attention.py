@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import POISON, decode_dev, say
+from gpu_common import POISON, decode_dev, record, say
 from moe_inputs import gen
 from oracle.attention import block_bytes, decode_attention
 from paged_moe_expert_amd import rimuru as R
@@ -39,10 +39,24 @@ def pack_blocks(K, V):
     return np.ascontiguousarray(bits).view(np.uint8).reshape(nb, -1)
 
 
-def setup(lens, n_kv, D, seed, expert_page=None, expert_every=1):
+def poison_tail(block: np.ndarray, L: int, n_kv: int, D: int) -> None:
+    """Fill the token slots at or past the context end L of a request's last
+    block (K rows and V columns of every KV head) with the pool's NaN filler."""
+    t0 = L % BT
+    if t0 == 0:
+        return
+    u = block.view(np.uint16)
+    kpart = u[:n_kv * BT * D].reshape(n_kv, BT, D)
+    vpart = u[n_kv * BT * D:].reshape(n_kv, D, BT)
+    kpart[:, t0:, :] = POISON & 0xFFFF
+    vpart[:, :, t0:] = POISON & 0xFFFF
+
+
+def setup(lens, n_kv, D, seed, expert_page=None, expert_every=1, stale_tails=False):
     """Allocator pool with an expert view and a KV view cut from it; expert
     owners (NaN pages) interleaved with the requests' KV blocks (one before
-    every expert_every-th request)."""
+    every expert_every-th request). stale_tails: the slots past each context
+    in its last block hold NaN instead of zeros."""
     bb = block_bytes(n_kv, D, "bf16")
     xp = expert_page or 4 * bb
     need = sum(-(-L // BT) for L in lens)
@@ -66,6 +80,8 @@ def setup(lens, n_kv, D, seed, expert_page=None, expert_every=1):
         K = rng.standard_normal((n_kv, L, D), dtype=np.float32)
         V = rng.standard_normal((n_kv, L, D), dtype=np.float32)
         blocks = pack_blocks(K, V)
+        if stale_tails:
+            poison_tail(blocks[-1], L, n_kv, D)
         for i, o in enumerate(offs):
             host[o:o + bb] = blocks[i]
     R.block_table_check(table, lens, bb, host.size)
@@ -89,6 +105,7 @@ def run_case(lens, n_q, n_kv, D, seed, sample=None, **kw):
     got = decode_dev(out)
     assert np.isfinite(got).all(), "read outside the request's blocks"
     reqs = list(range(B)) if sample is None else sample
+    worst = 0.0
     ref = decode_attention(qb, host, table, lens, n_q=n_q, n_kv=n_kv, head_dim=D, dtype="bf16",
                            scale=scale, requests=reqs)
     for i, b in enumerate(reqs):
@@ -97,7 +114,10 @@ def run_case(lens, n_q, n_kv, D, seed, sample=None, **kw):
             continue
         r = ref[i]
         err = (np.abs(got[b] - r).max(axis=1) / np.maximum(np.abs(r).max(axis=1), 1e-30)).max()
+        worst = max(worst, err)
         assert err <= 1e-2, f"request {b} (L={lens[b]}): rel_err {err:.3e}"
+    record(f"attention B={B} n_q={n_q} n_kv={n_kv} D={D}{' stale tails' if kw.get('stale_tails') else ''}",
+           worst, 1e-2)
     # a second call is bitwise equal (deterministic merge order)
     out2 = R.paged_decode_attention(q, pool, bt, lt, n_kv, scale)
     torch.cuda.synchronize()
@@ -108,6 +128,19 @@ def run_case(lens, n_q, n_kv, D, seed, sample=None, **kw):
 def test_ragged_lengths_qwen3_shape():
     lens = [1, 15, 16, 17, 33, 200, 700, 0, 5, 64, 129, 1000]
     assert run_case(lens, 32, 4, 128, seed=1) > 1
+
+
+def test_stale_nan_tails_of_last_blocks():
+    """The slots past each context in its last block hold the pool's NaN
+    filler (a block cut from a page that held something else): the output
+    stays finite and matches the oracle, with one split and with several."""
+    lens = [1, 15, 17, 31, 200, 701, 5, 1000, 33, 2047]
+    assert run_case(lens, 32, 4, 128, seed=21, stale_tails=True) > 1
+    rng = np.random.default_rng(22)
+    lens = np.clip(np.rint(rng.lognormal(4.5, 1.0, 256)), 1, 700).astype(int).tolist()
+    assert run_case(lens, 32, 4, 128, seed=23, sample=[0, 5, 64, 128, 255], expert_every=8,
+                    stale_tails=True) == 1
+    run_case([3, 250, 17], 16, 2, 256, seed=24, stale_tails=True)
 
 
 def test_one_long_request_many_splits():

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import decode_dev, rel_err, say, to_dev_bits, weights_dev
+from gpu_common import decode_dev, host_pool, record, rel_err, say, to_dev_bits, weights_dev
 from moe_inputs.configs import MoEConfig, ViewSpec
 from moe_inputs import gen
 from oracle.moe import moe_forward
@@ -87,10 +87,13 @@ def test_expert_upload_into_fresh_pages():
     b1 = R.fused_moe_paged(x, lgd, pool, torch.from_numpy(pt2).to(dev), page, k, I)
     torch.cuda.synchronize()
     assert torch.equal(b1.y, y0)                          # weights moved, results unchanged
-    pool_ref = pool_host.copy()
-    ref = moe_forward(xb, lg, pool_ref, pt2, page, E=E, k=k, H=H, I=I, dtype="bf16")
+    # the oracle's pool: the generator's weights placed on the host at the
+    # new page table's pages (nothing read back from the device)
+    ref = moe_forward(xb, lg, host_pool(cfg.pool_bytes, page, pt2, wb), pt2, page, E=E, k=k, H=H, I=I,
+                      dtype="bf16")
     err = rel_err(decode_dev(b1.y), ref["y"])
     say(f"[upload] rel_err vs oracle {err:.3e}")
+    record("expert upload, layer on the new pages", err, 1e-2)
     assert err <= 1e-2
 
     # eviction completes: the old pages return to the view
