@@ -303,6 +303,10 @@ def copy_foil_bench(args, cfg, x, lgd, pool, ptd, pt, bufs, dev, R, torch, np):
     expert's pages into one contiguous buffer (one device gather of whole
     pages), then runs the same layer on that buffer. The touched set is the
     one this input routes to (the same every step)."""
+    # the paged layer on the given logits first: its routing picks the
+    # experts to gather and its output is the one the foil must reproduce
+    R.fused_moe_paged(x, lgd, pool, ptd, cfg.page_bytes, cfg.k, cfg.I, bufs=bufs)
+    torch.cuda.synchronize()
     off = bufs.expert_off.cpu().numpy()
     srt = bufs.sorted_ids.cpu().numpy()
     TK = x.shape[0] * cfg.k
@@ -505,6 +509,11 @@ def measure(args, cfg, T, extras, dev, R, torch, np, gen):
             R.event_destroy(e)
     log(f"[bench] {cfg.name}: timed {args.steps} steps in {wall * 1e3:.2f} ms "
         f"({wall_events * 1e3:.2f} ms with stage events)")
+    # routing of the given logits, read back before any extra run reuses the buffers
+    off = bufs.expert_off.cpu().numpy()
+    srt = bufs.sorted_ids.cpu().numpy()
+    TK = T * cfg.k
+    counts = np.array([int(np.sum(srt[off[e]:off[e + 1]] < TK)) for e in range(cfg.E)])
 
     # Timed region 3: the same layer on a contiguous layout of the same weights
     # (pages consecutive and in order), for the cost of paging.
@@ -575,11 +584,7 @@ def measure(args, cfg, T, extras, dev, R, torch, np, gen):
             and any(v.name == "kv" for v in cfg.views) and any(name == "kv" for name, _ in lay.live):
         attn = attention_bench(args, cfg, lay, pool, dev, R, torch, np)
 
-    # ---- algorithmic work of this input
-    off = bufs.expert_off.cpu().numpy()
-    srt = bufs.sorted_ids.cpu().numpy()
-    TK = T * cfg.k
-    counts = np.array([int(np.sum(srt[off[e]:off[e + 1]] < TK)) for e in range(cfg.E)])
+    # ---- algorithmic work of this input (routing read back after the timed passes)
     touched = int(np.sum(counts > 0))
     es = cfg.es
     HI = cfg.H * cfg.I

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "librimuru.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in
-           ("allocator.cpp", "moe_routing.hip", "moe_gemm_stream.hip", "moe_gemm_tiled.hip",
+           ("allocator.cpp", "moe_routing.hip", "moe_gemm_stream.hip", "moe_gemm_tiled.hip", "moe_gemm_prefill.hip",
             "moe_layer.hip", "expert_upload.cpp", "adjuster.cpp", "attention.hip")]
 ARCH = "gfx950"
 

@@ -71,6 +71,46 @@ __device__ __forceinline__ float swap_lane_pair(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// ---------------------------------------------------------------- asynchronous copies and waits
+
+// vmcnt <= N (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their "no wait" values).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// lgkmcnt = 0 (LDS reads issued so far have returned).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which waits for
+// every load in flight, including the prefetched stages): callers wait for
+// exactly the loads they need first. The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds + 16*l; lds must be
+// wavefront-uniform. Issued through asm so the compiler does not order LDS
+// reads after it (it would wait for every copy in flight); callers wait with
+// wait_vmem. M0 is restored afterwards.
+__device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
 // ---------------------------------------------------------------- elements
 
 template <typename T>
@@ -250,6 +290,11 @@ constexpr int kStreamPtMax = 4096;
 // Few rows per expert (16-row tiles): weight-streaming GEMM.
 template <typename T, bool GATED>
 hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
+
+// Many rows per expert, bf16, 128-row tiles: the persistent pipelined GEMM;
+// hipErrorNotSupported when the shape is outside what it covers.
+template <bool GATED>
+hipError_t launch_prefill(const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
 
 // Many rows per expert (bm = 64 or 128): tiled MFMA GEMM.
 template <typename T, bool GATED>

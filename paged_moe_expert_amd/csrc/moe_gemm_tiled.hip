@@ -221,44 +221,6 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------- bf16, many rows: asynchronous pipeline
 
-// vmcnt <= N (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at their "no wait" values).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// lgkmcnt = 0 (LDS reads issued so far have returned).
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier without the memory fence of __syncthreads (which waits for
-// every load in flight, including the prefetched stages): callers wait for
-// exactly the loads they need first. The empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
-// lane l's 16 bytes land at LDS byte address lds + 16*l; lds must be
-// wavefront-uniform. Issued through asm so the compiler does not order LDS
-// reads after it (it would wait for every copy in flight); callers wait with
-// wait_vmem. M0 is restored afterwards.
-__device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds)
-      : "memory");
-}
-
 constexpr int kMtBM = 128;     // tile rows
 constexpr int kMtSN = 256;     // columns of one weight sub-tile (512-byte rows)
 #ifndef RIMURU_MT_GM
@@ -751,6 +713,10 @@ hipError_t launch_tiled(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream
   }
   if (bm != 128) return hipErrorInvalidValue;
   if constexpr (!kF32) {
+#ifndef RIMURU_PF_DISABLE
+    const hipError_t ep = launch_prefill<GATED>(g, tiles_max, st);
+    if (ep != hipErrorNotSupported) return ep;
+#endif
     const hipError_t e = launch_mt<GATED>(g, tiles_max, st);
     if (e != hipErrorNotSupported) return e;
     constexpr TileShape t = GATED ? kT128Up : kT128Dn;

@@ -76,6 +76,13 @@ CUSTOM = [
     ("bf16-pipelined-tiles", 8, 2, 512, 256, 1200, "bf16", 4 * KIB, None),
     ("bf16-pipelined-odd-page-skewed", 8, 2, 512, 512, 1500, "bf16", 12 * KIB, [3, 2, 1, 0, 0, 0, -1, -40]),
     ("bf16-pipelined-many-experts", 32, 4, 512, 256, 1400, "bf16", 64 * KIB, None),
+    # the persistent prefill GEMM: several tiles per workgroup (tile contexts
+    # and copies running on from one tile into the next), the shortest K it
+    # takes (6 stages), and 12 KiB pages whose boundaries cut 512-byte row
+    # pieces under skewed routing
+    ("bf16-pf-many-tiles", 8, 2, 512, 256, 40000, "bf16", 4 * KIB, None),
+    ("bf16-pf-short-k", 4, 2, 192, 256, 3000, "bf16", 4 * KIB, None),
+    ("bf16-pf-skewed-odd-page", 16, 4, 512, 512, 20000, "bf16", 12 * KIB, [4, 3, 2.5, 2, 1] + [0] * 9 + [-3, -50]),
     # the shape limits: 512 experts, top-32 (8 logits a lane in gating, a
     # 32-row combine), with a wavefront per token and with one-workgroup routing
     ("bf16-max-experts-and-k", 512, 32, 128, 64, 50, "bf16", 4 * KIB, None),
