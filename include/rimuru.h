@@ -396,6 +396,23 @@ rimuru_status rimuru_fused_moe_paged(const rimuru_moe_args* a, void* hip_stream)
 rimuru_status rimuru_fused_moe_paged_router(const rimuru_moe_args* a, const void* w_gate,
                                             float* logits_out, void* hip_stream);
 
+/* Bytes of the fixed device scratch rimuru_fused_moe_paged_noalloc uses as
+ * its workspace (one array per GPU, held until the process ends). */
+#define RIMURU_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* The same layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * it takes no workspace (a->workspace and a->workspace_bytes are ignored) and
+ * uses a fixed scratch array of RIMURU_NOALLOC_SCRATCH_BYTES on the current
+ * device instead; the caller still passes x, logits, the pool, pt and the
+ * outputs. It calls no allocating routine. Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (on different streams, or
+ * from several threads) race and must be ordered by the caller. The scratch
+ * needs no clearing between calls.
+ * Errors: ENOMEM (the shape's workspace, rimuru_moe_sizes' workspace_bytes,
+ * exceeds the scratch; nothing is enqueued), EINVAL, EDTYPE, EHIP. */
+rimuru_status rimuru_fused_moe_paged_noalloc(const rimuru_moe_args* a, void* hip_stream);
+
 /* Host-side check that every entry of a host copy of pt (E*3*P entries)
  * names a page inside a pool of pool_bytes bytes. ERANGE names the first bad
  * entry. */

@@ -16,6 +16,7 @@ OK, EINVAL, ENOMEM, ERANGE, EDTYPE, EHIP, EBUSY = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 VIEW_EXPERT, VIEW_KV, VIEW_SSM, VIEW_CONV = 0, 1, 2, 3
 MOE_STAGES = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20     # RIMURU_NOALLOC_SCRATCH_BYTES
 STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", ENOMEM: "ENOMEM", ERANGE: "ERANGE",
                 EDTYPE: "EDTYPE", EHIP: "EHIP", EBUSY: "EBUSY"}
 NO_BUDGET = (1 << 64) - 1
@@ -88,6 +89,7 @@ _PROTOS = {
                                                       C.POINTER(C.c_int32)]),
     "rimuru_fused_moe_paged": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p]),
     "rimuru_fused_moe_paged_router": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rimuru_fused_moe_paged_noalloc": (C.c_int32, [C.POINTER(MoeArgs), C.c_void_p]),
     "rimuru_pt_check": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_uint64, C.c_uint64]),
     "rimuru_experts_store": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_int32, C.c_int32,
                                          C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]),

@@ -9,6 +9,9 @@
 //   4 gemm-up    h = SiLU(x w1) * (x w3), w1/w3 read through the page table
 //   5 gemm-down  y_slot[t*k+j] = w[t,j] * (h w2), w2 through the page table
 //   6 combine    y[t] = sum_j y_slot[t*k+j], j in rank order
+#include <atomic>
+#include <mutex>
+
 #include "moe_common.h"
 
 namespace rimuru {
@@ -212,6 +215,71 @@ extern "C" rimuru_status rimuru_fused_moe_paged_router(const rimuru_moe_args* a,
     return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_router: w_gate must be a 16-byte aligned device pointer");
   RouterArgs r{a->x, w_gate, a->H, a->dtype == RIMURU_BF16, logits_out};
   return run_layer(a, &r, hip_stream);   // logits_out == NULL: run_layer points it at the workspace
+}
+
+// ---------------------------------------------------------------- the layer without a caller workspace
+
+// Scratch of rimuru_fused_moe_paged_noalloc: the layer's workspace (tile map,
+// router logits, h, y_slot) in a fixed device array, for callers that cannot
+// allocate. Every GPU the library runs on holds its own copy until the process
+// ends. In host code the array's name is not a device address: its address on
+// a device comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept below. Nothing in the workspace has to start at
+// zero (every kernel writes what it later reads), so the scratch is never
+// cleared.
+namespace rimuru {
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[RIMURU_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+rimuru_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return rimuru_fail(RIMURU_EHIP, "fused_moe_paged_noalloc: hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_noalloc: device %d beyond the %d this library tracks", dev, kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (err != hipSuccess || p == nullptr)
+        return rimuru_fail(RIMURU_EHIP, "fused_moe_paged_noalloc: hipGetSymbolAddress of the scratch on device %d: %s",
+                           dev, hipGetErrorString(err));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RIMURU_OK;
+}
+
+}  // namespace
+}  // namespace rimuru
+
+extern "C" rimuru_status rimuru_fused_moe_paged_noalloc(const rimuru_moe_args* a, void* hip_stream) {
+  if (a == nullptr) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_noalloc: args is NULL");
+  rimuru_status s = check_shapes(a->T, a->E, a->k, a->H, a->I, a->dtype);
+  if (s != RIMURU_OK) return s;
+  if (a->T == 0) return RIMURU_OK;
+  if (a->P < 1) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_noalloc: P = %d must be at least 1", a->P);
+  const Plan p = choose_plan(a->T, a->E, a->k, a->P);
+  const Layout lay = layout_for(a->T, a->E, a->k, a->H, a->I, a->dtype == RIMURU_BF16 ? 2 : 4, p.bm);
+  if (lay.total > RIMURU_NOALLOC_SCRATCH_BYTES)
+    return rimuru_fail(RIMURU_ENOMEM, "fused_moe_paged_noalloc: this shape needs %llu bytes of workspace, above the "
+                       "%llu-byte scratch of the no-allocation entry point (use rimuru_fused_moe_paged with a "
+                       "workspace)", (unsigned long long)lay.total, (unsigned long long)RIMURU_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if ((s = scratch_of_current_device(&ptr)) != RIMURU_OK) return s;
+  rimuru_moe_args b = *a;
+  b.workspace = ptr;
+  b.workspace_bytes = RIMURU_NOALLOC_SCRATCH_BYTES;
+  return run_layer(&b, nullptr, hip_stream);
 }
 
 extern "C" rimuru_status rimuru_pt_check(const int32_t* pt_host, int32_t E, int32_t P,

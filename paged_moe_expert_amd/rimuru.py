@@ -9,7 +9,8 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, EBUSY, EINVAL, ENOMEM, ERANGE, AdjusterParams,  # noqa: F401
+from ._lib import (BF16, F32, MOE_STAGES, NO_BUDGET, NOALLOC_SCRATCH_BYTES, EBUSY, EINVAL, ENOMEM, ERANGE,  # noqa: F401
+                   AdjusterParams,
                    AttnArgs, MoeArgs, OK, PoolStats, RimuruError, check, lib)
 
 
@@ -205,9 +206,11 @@ def moe_sizes(T: int, E: int, k: int, H: int, I: int, P: int, dtype: int):
 
 
 class MoeBuffers:
-    """Outputs and workspace for one shape; reuse them across calls."""
+    """Outputs and workspace for one shape; reuse them across calls.
+    workspace=False leaves the workspace out (the no-allocation entry point
+    brings its own)."""
 
-    def __init__(self, T, E, k, H, I, P, dtype, device="cuda"):
+    def __init__(self, T, E, k, H, I, P, dtype, device="cuda", workspace=True):
         import torch
         tdt = torch.bfloat16 if dtype == BF16 else torch.float32
         sl, ws, bm = moe_sizes(T, E, k, H, I, P, dtype)
@@ -218,7 +221,8 @@ class MoeBuffers:
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
         self.sorted_ids = torch.empty(max(sl, 1), dtype=torch.int32, device=device)
         self.expert_off = torch.empty(E + 1, dtype=torch.int32, device=device)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.workspace_bytes = ws
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device) if workspace else None
 
 
 def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
@@ -249,6 +253,8 @@ def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
     a.page_bytes = page_bytes
     a.y, a.topk_ids, a.topk_w = bufs.y.data_ptr(), bufs.topk_ids.data_ptr(), bufs.topk_w.data_ptr()
     a.sorted_ids, a.expert_off = bufs.sorted_ids.data_ptr(), bufs.expert_off.data_ptr()
+    if bufs.workspace is None:
+        raise ValueError("fused_moe_paged: these buffers have no workspace (made for fused_moe_paged_noalloc)")
     a.workspace, a.workspace_bytes = bufs.workspace.data_ptr(), bufs.workspace.numel()
     ev_arr = None
     if stage_events is not None:
@@ -264,6 +270,29 @@ def fused_moe_paged(x, logits, pool, pt, page_bytes: int, k: int, I: int,
         out = logits_out.data_ptr() if logits_out is not None else None
         check(lib().rimuru_fused_moe_paged_router(C.byref(a), w_gate.data_ptr(), out, s.cuda_stream),
               "fused_moe_paged_router")
+    return bufs
+
+
+def fused_moe_paged_noalloc(x, logits, pool, pt, page_bytes: int, k: int, I: int,
+                            bufs: MoeBuffers | None = None, stream=None) -> MoeBuffers:
+    """rimuru_fused_moe_paged_noalloc: the layer with the library's fixed
+    device scratch as its workspace (no workspace argument). bufs holds the
+    outputs only (MoeBuffers(..., workspace=False))."""
+    import torch
+    T, H = x.shape
+    E = logits.shape[1]
+    P = pt.shape[2]
+    dt = _dtype_code(x)
+    if bufs is None:
+        bufs = MoeBuffers(T, E, k, H, I, P, dt, device=x.device, workspace=False)
+    a = MoeArgs()
+    a.T, a.E, a.k, a.H, a.I, a.P, a.dtype, a.renormalize = T, E, k, H, I, P, dt, 1
+    a.x, a.logits, a.pool_base, a.pt = x.data_ptr(), logits.data_ptr(), pool.data_ptr(), pt.data_ptr()
+    a.page_bytes = page_bytes
+    a.y, a.topk_ids, a.topk_w = bufs.y.data_ptr(), bufs.topk_ids.data_ptr(), bufs.topk_w.data_ptr()
+    a.sorted_ids, a.expert_off = bufs.sorted_ids.data_ptr(), bufs.expert_off.data_ptr()
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    check(lib().rimuru_fused_moe_paged_noalloc(C.byref(a), s.cuda_stream), "fused_moe_paged_noalloc")
     return bufs
 
 
