@@ -688,7 +688,7 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="headline configuration (default: the 8192-token "
                                                            "fragmented prefill)")
     ap.add_argument("--nested", default="2,3",
-                    help="other configurations measured in the same run, nested in the line ('' = none)")
+                    help="other configurations measured in the same run, nested in the line ('none' or '' = none)")
     ap.add_argument("--tokens", type=int, default=0, help="override T of the headline (decode sweep)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
@@ -739,7 +739,9 @@ def main():
     head = measure(args, cfg, T, extras | ({"cpu"} if not args.no_cpu else set()), dev, R, torch, np, gen)
 
     nested = {}
-    for tok in filter(None, (t.strip() for t in args.nested.split(","))):
+    for tok in filter(None, (t.strip().strip("'\"") for t in args.nested.split(","))):
+        if tok == "none":
+            continue
         cid = int(tok)
         if cid == args.config:
             continue

@@ -52,10 +52,20 @@ constexpr StreamNarrow kStreamNarrow{RIMURU_STREAM_NARROW};
 // expert) 280.6k -> 321.6k tokens/s; 16 tokens 152 -> 138 us cache-cold;
 // 256 tokens (16 rows, many experts two row tiles) 1.5% slower cache-cold.
 constexpr int kStreamNtRows = 8;
+// load policy above kStreamNtRows rows per expert: 2 = per expert, 0 = plain
+#ifndef RIMURU_STREAM_NT_MIXED
+#define RIMURU_STREAM_NT_MIXED 2
+#endif
 struct StreamShape { int bn, depth; };
 constexpr StreamShape kStreamUp{RIMURU_STREAM_UP}, kStreamDn{RIMURU_STREAM_DN};
 constexpr int kStreamUpBN = kStreamUp.bn, kStreamUpDepth = kStreamUp.depth;
 constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
+
+// LDS of one streaming wavefront (its weight slice, then its partial sums)
+template <typename T, int BN, bool GATED>
+constexpr int stream_wave_lds() {
+  return (GATED ? 2 : 1) * kStreamK * (BN + Elt<T>::B_PAD);
+}
 
 // NSTEPS > 0: the wavefront's step count is known at compile time and the K
 // loop unrolls into straight-line code (a loop back-edge makes the compiler
@@ -67,8 +77,12 @@ constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
 // read of HBM measured 6.9 TB/s with non-temporal loads against 6.2 TB/s
 // with plain ones; taken when each expert's weights are read by one row tile
 // (few routed rows per expert), where nothing re-reads them in the launch.
+// One workgroup's tile (row tile mt, column tile nt of expert e). lds holds
+// kStreamMaxWaves wavefront slices of stream_wave_lds elements; pt_lds the
+// expert's page-table rows (NB * P) when not ONE_PAGE.
 template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, bool NT>
-__global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
+__device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int mt, int nt, int e, T* lds,
+                                            int32_t* pt_lds) {
   typedef Elt<T> X;
   constexpr int NB = GATED ? 2 : 1;
   constexpr int VEC = X::VEC;
@@ -78,23 +92,9 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   constexpr int TN = BN / 16;
   constexpr int BNP = BN + X::B_PAD;           // row pitch of the wave's weight slice
   constexpr int SEG8 = X::SEG8;
+  constexpr int WL = stream_wave_lds<T, BN, GATED>();
   static_assert(CG * RG == 64 && RPL * RG == kStreamK, "stream tile shape");
-  static_assert(NB * 16 * BN * 4 <= NB * kStreamK * BNP * X::ES, "reduction must fit the wave buffer");
-
-  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves][NB * kStreamK * BNP];
-  extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
-
-  const int nN = a.N / BN;
-  const int n_tiles = a.expert_off[a.E] / 16;
-  const int L = n_tiles * nN;
-  const int chunk = (L + 7) >> 3;
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  if (idx >= chunk) return;
-  const int logical = xcd * chunk + idx;
-  if (logical >= L) return;
-  const int mt = logical / nN;
-  const int nt = logical - mt * nN;
-  const int e = a.tile_expert[mt];
+  static_assert(NB * 16 * BN * 4 <= WL * X::ES, "reduction must fit the wave buffer");
   const int r0 = mt * 16;
   const int n0 = nt * BN;
 
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  T* wbuf = lds[wv];
+  T* wbuf = lds + wv * WL;
 
   // Loads of step st (clamped to the last step: the surplus loads at the end
   // repeat addresses already in cache and their data is never used).
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
 #pragma unroll
       for (int c = 0; c < PER; ++c) v[b][c] = 0.0f;
     for (int w = 0; w < ksplit; ++w) {
-      const float* rw = reinterpret_cast<const float*>(lds[w]);
+      const float* rw = reinterpret_cast<const float*>(lds + w * WL);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -265,11 +265,40 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   }
 }
 
+// NT_MODE 0: plain weight loads, 1: non-temporal, 2: per expert --
+// non-temporal when the expert's rows are one tile (nothing else in the
+// launch reads its weights), plain when several row tiles share them.
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, int NT_MODE>
+__global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
+  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves * stream_wave_lds<T, BN, GATED>()];
+  extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
+
+  const int nN = a.N / BN;
+  const int n_tiles = a.expert_off[a.E] / 16;
+  const int L = n_tiles * nN;
+  const int chunk = (L + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  if (idx >= chunk) return;
+  const int logical = xcd * chunk + idx;
+  if (logical >= L) return;
+  const int mt = logical / nN;
+  const int nt = logical - mt * nN;
+  const int e = a.tile_expert[mt];
+  if constexpr (NT_MODE == 2) {
+    if (a.expert_off[e + 1] - a.expert_off[e] == 16)
+      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, true>(a, ksplit, mt, nt, e, lds, pt_lds);
+    else
+      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, false>(a, ksplit, mt, nt, e, lds, pt_lds);
+  } else {
+    stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, NT_MODE == 1>(a, ksplit, mt, nt, e, lds, pt_lds);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 namespace {
 
-template <typename T, int BN, int DEPTH, bool GATED, bool ONE_PAGE, bool NT>
+template <typename T, int BN, int DEPTH, bool GATED, bool ONE_PAGE, int NT>
 void launch_stream_steps(int steps, dim3 gd, dim3 bd, size_t lds, hipStream_t st, const GemmArgs& g, int ksplit) {
   switch (steps) {
 #define RIMURU_STREAM_CASE(n) \
@@ -298,15 +327,17 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
   if (grid == 0) return hipSuccess;
   const dim3 gd(static_cast<uint32_t>(grid)), bd(ksplit * 64);
   // at most kStreamNtRows routed rows per expert on average: most experts
-  // are one row tile, read once, so the weights stream past the caches
-  const bool nt = static_cast<int64_t>(g.TK) <= static_cast<int64_t>(kStreamNtRows) * g.E;
+  // are one row tile, read once, so the weights stream past the caches;
+  // above that the choice is made per expert (non-temporal for experts whose
+  // rows are one tile, plain loads where several row tiles share weights)
+  const bool all_nt = static_cast<int64_t>(g.TK) <= static_cast<int64_t>(kStreamNtRows) * g.E;
   const size_t pt_bytes = g.P == 1 ? 0 : static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
   if (g.P == 1) {
-    if (nt) launch_stream_steps<T, BN, DEPTH, GATED, true, true>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
-    else launch_stream_steps<T, BN, DEPTH, GATED, true, false>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
+    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, true, 1>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
+    else launch_stream_steps<T, BN, DEPTH, GATED, true, RIMURU_STREAM_NT_MIXED>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
   } else {
-    if (nt) launch_stream_steps<T, BN, DEPTH, GATED, false, true>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
-    else launch_stream_steps<T, BN, DEPTH, GATED, false, false>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
+    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, false, 1>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
+    else launch_stream_steps<T, BN, DEPTH, GATED, false, RIMURU_STREAM_NT_MIXED>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
   }
   return hipGetLastError();
 }

@@ -28,10 +28,13 @@ struct Plan {
   int bm;
 };
 
+#ifndef RIMURU_PLAN64_MAX_ROWS
+#define RIMURU_PLAN64_MAX_ROWS 160
+#endif
 Plan choose_plan(int64_t T, int E, int k, int64_t P) {
   int64_t tk = T * k;
   if (tk <= 24ll * E && 2 * P <= kStreamPtMax) return {kPlan16, 16};
-  if (tk <= 160ll * E) return {kPlan64, 64};
+  if (tk <= static_cast<int64_t>(RIMURU_PLAN64_MAX_ROWS) * E) return {kPlan64, 64};
   return {kPlan128, 128};
 }
 
