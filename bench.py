@@ -33,7 +33,10 @@ CSRC = os.path.join(ROOT, "paged_moe_expert_amd", "csrc")
 # sources each GEMM kernel is compiled from: a traffic measurement stays valid
 # while these are unchanged
 KERNEL_SOURCES = {"stream": ("moe_common.h", "moe_gemm_stream.hip"),
-                  "tiled": ("moe_common.h", "moe_gemm_tiled.hip")}
+                  "tiled": ("moe_common.h", "moe_gemm_tiled.hip"),
+                  "prefill": ("moe_common.h", "moe_gemm_prefill.hip")}
+# GEMM kernel family of each tile height
+KIND_OF_BLOCK_M = {16: "stream", 64: "tiled", 128: "prefill"}
 STAGES = ["gating", "count", "sort", "gemm_up", "gemm_down", "combine"]
 
 
@@ -605,7 +608,7 @@ def measure(args, cfg, T, extras, dev, R, torch, np, gen):
     med = np.median(stage_ms, axis=0)
     mean = stage_ms.mean(axis=0)
     decode_like = (w_bytes + io_bytes) / HBM_PEAK_GBS > flops / (BF16_PEAK_TFLOPS * 1e3)
-    kind = "stream" if bufs.block_m == 16 else "tiled"
+    kind = KIND_OF_BLOCK_M.get(bufs.block_m, "tiled")
 
     def kernel_roof(name, ms, nbytes, nflops, traffic):
         if decode_like:

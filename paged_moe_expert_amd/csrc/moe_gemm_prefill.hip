@@ -75,26 +75,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // tile) in its L2.
   const int nN = a.N / BNW;
   const int L = (a.expert_off[a.E] / kPfBM) * nN;
-#ifndef RIMURU_PF_MAP
-#define RIMURU_PF_MAP 0
-#endif
-#if RIMURU_PF_MAP == 0
   const int wpx = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7;
   const int chunk = (L + 7) >> 3;
   const int t_end = min((xcd + 1) * chunk, L);
   int t = xcd * chunk + (blockIdx.x >> 3);
-#elif RIMURU_PF_MAP == 1
-  const int wpx = gridDim.x >> 3;
-  const int xcd = blockIdx.x / wpx;
-  const int chunk = (L + 7) >> 3;
-  const int t_end = min((xcd + 1) * chunk, L);
-  int t = xcd * chunk + (blockIdx.x % wpx);
-#else
-  const int wpx = gridDim.x;
-  const int t_end = L;
-  int t = blockIdx.x;
-#endif
   if (t >= t_end) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
