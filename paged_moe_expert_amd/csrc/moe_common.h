@@ -291,10 +291,10 @@ constexpr int kStreamPtMax = 4096;
 template <typename T, bool GATED>
 hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
 
-// Many rows per expert, bf16, 128-row tiles: the persistent pipelined GEMM;
-// hipErrorNotSupported when the shape is outside what it covers.
+// Many rows per expert, bf16, 64- or 128-row tiles: the persistent pipelined
+// GEMM; hipErrorNotSupported when the shape is outside what it covers.
 template <bool GATED>
-hipError_t launch_prefill(const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
+hipError_t launch_prefill(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
 
 // Many rows per expert (bm = 64 or 128): tiled MFMA GEMM.
 template <typename T, bool GATED>

@@ -21,16 +21,15 @@
 
 namespace rimuru {
 
-constexpr int kPfBM = 128;        // tile rows
 constexpr int kPfSN = 256;        // columns of one weight sub-tile (512-byte rows)
 constexpr int kPfBK = 32;         // K rows per stage
 constexpr int kPfStages = 3;      // stages in the LDS ring
 constexpr int kPfCtxPages = 1024; // page addresses a tile context holds
 
-template <int NW>
+template <int NW, int BM>
 struct PfShape {
   static constexpr int KS = kPfBK / 16;                  // MFMA K steps per stage
-  static constexpr int A_CHUNKS = (kPfBM / 32) * KS;     // 1 KB chunks of A per stage
+  static constexpr int A_CHUNKS = (BM / 32) * KS;        // 1 KB chunks of A per stage
   static constexpr int A_BYTES = A_CHUNKS * 1024;
   static constexpr int SUB_CHUNKS = kPfBK * kPfSN * 2 / 1024;  // 2-row chunks of one sub-tile
   static constexpr int CHUNK_PITCH = 1024 + 64;          // padded: 4 rows of a transpose read in 4 bank phases
@@ -41,32 +40,35 @@ struct PfShape {
   static constexpr int B_DMA = 2 * SUB_CHUNKS / NW;
   static constexpr int DMA = A_DMA + B_DMA;
   static constexpr int WGM = NW / 4;                     // wavefront row groups (x 4 column groups)
-  static constexpr int TM = 4 / WGM;                     // 32-row blocks per wavefront
+  static constexpr int TM = BM / 32 / WGM;               // 32-row blocks per wavefront
   static constexpr int NMMA = TM * 4;                    // MFMAs per K step
   static constexpr int NREAD = TM + 8;                   // operand reads per K step
   static constexpr int OPR = kPfBK / 8;                  // 16-byte K octets per A row
   static constexpr int RPC = 64 / OPR;                   // A rows per copy
   static_assert(NW == 4 || NW == 8, "one or two wavefronts per SIMD");
+  static_assert((BM == 128 || BM == 64) && TM >= 1, "tile rows");
   static_assert(A_CHUNKS % NW == 0 && (2 * SUB_CHUNKS) % NW == 0 && KS == 2, "copy split");
   static_assert(2 * DMA < 64, "copies in flight");
 };
 
 // What a workgroup knows about one tile, in LDS (two: the tile being
 // computed and the next one, filled while the current one runs).
+template <int BM>
 struct PfCtx {
-  int32_t slot[kPfBM];            // routed slot of each row (>= TK: padding)
-  float w[kPfBM];                 // routing weight of each row (down GEMM)
+  int32_t slot[BM];               // routed slot of each row (>= TK: padding)
+  float w[BM];                    // routing weight of each row (down GEMM)
   int32_t r0, n0, pad[2];         // first sorted row, first output column
   uint64_t page[kPfCtxPages];     // pool address of each page of the tile's projections
 };
 
-template <bool GATED, int NW>
+template <bool GATED, int NW, int BM>
 __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
-  typedef PfShape<NW> S;
+  typedef PfShape<NW, BM> S;
+  typedef PfCtx<BM> Ctx;
   constexpr int NBM = GATED ? 2 : 1;              // weight matrices read
   constexpr int BNW = 2 * kPfSN / NBM;            // output columns per tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfStages * S::STAGE_BYTES];
-  __shared__ PfCtx ctx[2];
+  __shared__ Ctx ctx[2];
 
   // ---- this workgroup's tiles: XCD x (dispatch deals workgroups to the 8
   // XCDs in turn) owns a contiguous chunk of the live tiles, walked by its
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // columns (row tiles of one expert) and x rows (column tiles of one row
   // tile) in its L2.
   const int nN = a.N / BNW;
-  const int L = (a.expert_off[a.E] / kPfBM) * nN;
+  const int L = (a.expert_off[a.E] / BM) * nN;
   const int wpx = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7;
   const int chunk = (L + 7) >> 3;
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   auto prep_load = [&](int tt, Prep& p) {
     const int mt = tt / nN, nt = tt - mt * nN;
     const int e = a.tile_expert[mt];
-    p.r0 = mt * kPfBM;
+    p.r0 = mt * BM;
     p.n0 = nt * BNW;
 #pragma unroll
     for (int j = 0; j < PREP; ++j) {
@@ -113,18 +115,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
     }
     p.slot = a.TK;
     p.w = 0.0f;
-    if (tid < kPfBM) {
+    if (tid < BM) {
       p.slot = a.sorted_ids[p.r0 + tid];
       if (!GATED && p.slot < a.TK) p.w = a.topk_w[p.slot];
     }
   };
-  auto prep_store = [&](PfCtx& c, const Prep& p) {
+  auto prep_store = [&](Ctx& c, const Prep& p) {
 #pragma unroll
     for (int j = 0; j < PREP; ++j) {
       const int i = tid + j * S::NT;
       if (i < np) c.page[i] = reinterpret_cast<uint64_t>(a.pool) + static_cast<uint64_t>(p.pg[j]) * page;
     }
-    if (tid < kPfBM) {
+    if (tid < BM) {
       c.slot[tid] = p.slot;
       c.w[tid] = p.w;
     }
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // A weight segment's pool address is the address of its page (LDS, the
   // tile context) plus its offset in the page.
   struct Src { const uint8_t* a[S::A_DMA]; uint32_t f[S::B_DMA]; };
-  auto sources = [&](const PfCtx& c, Src& s) {
+  auto sources = [&](const Ctx& c, Src& s) {
 #pragma unroll
     for (int d = 0; d < S::A_DMA; ++d) {
       const int trow = (w * S::A_DMA + d) * S::RPC + lane / S::OPR;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // The page address and the offset stay apart until the copy: adding them
   // at lookup time would make the wavefront wait for the LDS read there.
   struct Refill { uint64_t pb[S::B_DMA]; uint32_t rem[S::B_DMA]; };
-  auto lookup_one = [&](const PfCtx& c, const Src& s, int rst, Refill& r, int d) {
+  auto lookup_one = [&](const Ctx& c, const Src& s, int rst, Refill& r, int d) {
     const uint32_t f = s.f[d] + static_cast<uint32_t>(rst) * stage_step;
     const uint32_t q = page_index(f, a.pd);
     r.pb[d] = c.page[bmat(d) * a.P + q];
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
     constexpr int vm = decltype(VM)::value;
     constexpr int more_k = decltype(MORE)::value;
     constexpr bool more = more_k > 0, read_next = more_k > 1;
-    const PfCtx& rc = ctx[(rk == 2) ? (cidx ^ 1) : cidx];
+    const Ctx& rc = ctx[(rk == 2) ? (cidx ^ 1) : cidx];
     const Src& rs = (rk == 2) ? nxt : cur;
     const int nbuf = buf == kPfStages - 1 ? 0 : buf + 1;
     const uint32_t buf_lds = smem_lds + buf * S::STAGE_BYTES;   // refill target: this stage's slot
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   auto store2 = [&](uint32_t off, float lo, float hi) {
     *reinterpret_cast<uint32_t*>(Cb + off) = pack_bf16x2(lo, hi);
   };
-  auto epilogue = [&](const PfCtx& c) {
+  auto epilogue = [&](const Ctx& c) {
     const uint32_t colb = static_cast<uint32_t>(c.n0 + 64 * wn + (lane & 31) - (odd ? 1 : 0)) * 2;
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
@@ -434,31 +436,34 @@ int cu_count() {
 }
 }  // namespace
 
-#ifndef RIMURU_PF_WAVES
-#define RIMURU_PF_WAVES 8
-#endif
-
+// 128-row tiles: 8 wavefronts (two per SIMD, 64 rows x 128 columns each);
+// 64-row tiles: 4 wavefronts (one per SIMD, the same 64 x 128 each), for
+// the down projection of weight-bound layers (few rows per expert): its
+// tiles carry half the padding and the copies, not the MFMAs, set its pace.
 template <bool GATED>
-hipError_t launch_prefill(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+hipError_t launch_prefill(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   const int nbm = GATED ? 2 : 1;
   const int bnw = 2 * kPfSN / nbm;
+  if (bm != 128 && (bm != 64 || GATED)) return hipErrorNotSupported;
   // shapes this kernel covers: whole column tiles, whole stages, at least
   // five stages (the first and the last three are peeled, and the next
   // tile's context needs one barrier between them), page addresses of a tile
   // within one context
-  const uint64_t out_rows = GATED ? tiles_max * kPfBM : static_cast<uint64_t>(g.TK);
+  const uint64_t out_rows = GATED ? tiles_max * bm : static_cast<uint64_t>(g.TK);
   if (g.N % bnw != 0 || g.K % kPfBK != 0 || g.K / kPfBK < 5 || nbm * g.P > kPfCtxPages ||
       out_rows * static_cast<uint64_t>(g.ldc) * 2 >= (1ull << 32))
     return hipErrorNotSupported;
   const uint64_t tiles = tiles_max * static_cast<uint64_t>(g.N / bnw);
   uint64_t grid = std::min<uint64_t>(static_cast<uint64_t>(cu_count() / 8 * 8), (tiles + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_moe_gemm_pf<GATED, RIMURU_PF_WAVES>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(RIMURU_PF_WAVES * 64), 0, st, g);
+  if (bm == 128)
+    hipLaunchKernelGGL((k_moe_gemm_pf<GATED, 8, 128>), dim3(static_cast<uint32_t>(grid)), dim3(8 * 64), 0, st, g);
+  else if constexpr (!GATED)
+    hipLaunchKernelGGL((k_moe_gemm_pf<GATED, 4, 64>), dim3(static_cast<uint32_t>(grid)), dim3(4 * 64), 0, st, g);
   return hipGetLastError();
 }
 
-template hipError_t launch_prefill<true>(const GemmArgs&, uint64_t, hipStream_t);
-template hipError_t launch_prefill<false>(const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_prefill<true>(int, const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_prefill<false>(int, const GemmArgs&, uint64_t, hipStream_t);
 
 }  // namespace rimuru

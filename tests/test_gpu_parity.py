@@ -83,6 +83,9 @@ CUSTOM = [
     ("bf16-pf-many-tiles", 8, 2, 512, 256, 40000, "bf16", 4 * KIB, None),
     ("bf16-pf-short-k", 4, 2, 192, 256, 3000, "bf16", 4 * KIB, None),
     ("bf16-pf-skewed-odd-page", 16, 4, 512, 512, 20000, "bf16", 12 * KIB, [4, 3, 2.5, 2, 1] + [0] * 9 + [-3, -50]),
+    # the persistent GEMM on 64-row tiles (few rows per expert, weight-bound)
+    ("bf16-pf64-tiles", 64, 8, 512, 256, 1000, "bf16", 8 * KIB, None),
+    ("bf16-pf64-skewed-odd-page", 32, 4, 512, 512, 1200, "bf16", 12 * KIB, [3, 2, 1.5, 1] + [0] * 26 + [-2, -40]),
     # the shape limits: 512 experts, top-32 (8 logits a lane in gating, a
     # 32-row combine), with a wavefront per token and with one-workgroup routing
     ("bf16-max-experts-and-k", 512, 32, 128, 64, 50, "bf16", 4 * KIB, None),
