@@ -37,12 +37,20 @@ CASES = [
     ("f32-router", 8, 2, 128, 64, 33, "f32", 4 * KIB),
     ("bf16-router-decode-shape", 128, 8, 2048, 768, 64, "bf16", 3 * 1024 * KIB),
     ("bf16-router-prefill-tiles", 16, 4, 512, 256, 1200, "bf16", 16 * KIB),
-    # enough token blocks for the wider expert tiles of the router GEMM
-    # (32, 64 and 128 experts per workgroup), each with a ragged token tail
-    ("bf16-router-nt2", 128, 8, 128, 64, 4100, "bf16", 8 * KIB),
-    ("bf16-router-nt4", 128, 8, 128, 64, 8200, "bf16", 8 * KIB),
-    ("bf16-router-nt8", 128, 8, 128, 64, 16400, "bf16", 8 * KIB),
+    # register-operand router GEMM (fp32 inputs): enough token blocks for
+    # its wider expert tiles (32, 64 and 128 experts per workgroup), each
+    # with a ragged token tail
+    ("f32-router-nt2", 128, 8, 128, 64, 4100, "f32", 8 * KIB),
+    ("f32-router-nt4", 128, 8, 128, 64, 8200, "f32", 8 * KIB),
     ("f32-router-nt8-E64", 64, 4, 128, 64, 16400, "f32", 8 * KIB),   # tile wider than E
+    # LDS-staged router GEMM (bf16, H a multiple of 64, a workgroup per CU):
+    # 128, 64 and 32 experts per workgroup (no K split, 2-way, 4-way), a
+    # ragged token tail, an expert tile past E, a one-stage K loop, and the
+    # 8192-token prefill's router shape
+    ("bf16-router-wide-ne4-E200", 200, 8, 512, 64, 4100, "bf16", 8 * KIB),
+    ("bf16-router-wide-ne2", 128, 8, 192, 64, 4100, "bf16", 8 * KIB),
+    ("bf16-router-wide-ne1-one-stage", 40, 6, 64, 64, 4100, "bf16", 8 * KIB),
+    ("bf16-router-prefill-shape", 128, 8, 2048, 64, 8192, "bf16", 64 * KIB),
 ]
 
 
