@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "paged_moe_expert_amd", "csrc")
 KERNEL_SOURCES = {"stream": ("moe_common.h", "moe_gemm_stream.hip"),
                   "tiled": ("moe_common.h", "moe_gemm_tiled.hip"),
                   "prefill": ("moe_common.h", "moe_gemm_prefill.hip")}
-# GEMM kernel family of each tile height
-KIND_OF_BLOCK_M = {16: "stream", 64: "tiled", 128: "prefill"}
+# GEMM kernel family (gate/up, down) of each tile height
+KIND_OF_BLOCK_M = {16: ("stream", "stream"), 64: ("tiled", "prefill"), 128: ("prefill", "prefill")}
 STAGES = ["gating", "count", "sort", "gemm_up", "gemm_down", "combine"]
 
 
@@ -608,7 +608,7 @@ def measure(args, cfg, T, extras, dev, R, torch, np, gen):
     med = np.median(stage_ms, axis=0)
     mean = stage_ms.mean(axis=0)
     decode_like = (w_bytes + io_bytes) / HBM_PEAK_GBS > flops / (BF16_PEAK_TFLOPS * 1e3)
-    kind = KIND_OF_BLOCK_M.get(bufs.block_m, "tiled")
+    kind_up, kind_dn = KIND_OF_BLOCK_M.get(bufs.block_m, ("tiled", "tiled"))
 
     def kernel_roof(name, ms, nbytes, nflops, traffic):
         if decode_like:
@@ -623,9 +623,9 @@ def measure(args, cfg, T, extras, dev, R, torch, np, gen):
                 "avg_launch_us": round(ms * 1e3, 2)}
 
     roof = kernel_roof("gemm_up", float(mean[3]), up_bytes, up_flops,
-                       traffic_from_profiles(cfg.name, "gemm_up", kind))
+                       traffic_from_profiles(cfg.name, "gemm_up", kind_up))
     roof_dn = kernel_roof("gemm_down", float(mean[4]), dn_bytes, dn_flops,
-                          traffic_from_profiles(cfg.name, "gemm_down", kind))
+                          traffic_from_profiles(cfg.name, "gemm_down", kind_dn))
     layer_roof_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), (w_bytes + io_bytes) / (HBM_PEAK_GBS * 1e9)) * 1e6
     out = {
         "value": round(T / (ms_step * 1e-3), 1),
