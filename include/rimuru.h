@@ -437,7 +437,8 @@ rimuru_status rimuru_experts_store(void* pool_base, uint64_t pool_bytes, const i
 /* Elastic expert offloading, dual-buffer upload (Rimuru paper summary,
  * Figure 8: expert prefetch overlapped with execution, no device-to-device
  * copy): copy one expert's three projections from host memory straight into
- * fresh expert-view pages, one host-to-device copy per page, on hip_stream
+ * fresh expert-view pages, one host-to-device copy per run of pages that are
+ * consecutive in the pool and in the projection, on hip_stream
  * (typically a copy stream beside the stream running the layer). The pages
  * are written where they sit; since the layer reads every weight through the
  * page table, the expert is usable as soon as its page-table rows name these

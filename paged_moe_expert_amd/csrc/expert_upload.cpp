@@ -1,8 +1,8 @@
 // Dual-buffer expert upload (Rimuru paper summary, Figure 8): an evicted
-// expert comes back from host memory directly into fresh expert-view pages,
-// one asynchronous host-to-device copy per page on the caller's stream, so
-// the upload overlaps the layer running on another stream and no staging
-// buffer or device-to-device copy is involved.
+// expert comes back from host memory directly into fresh expert-view pages
+// by asynchronous host-to-device copies on the caller's stream (one per run
+// of consecutive pages), so the upload overlaps the layer running on another
+// stream and no staging buffer or device-to-device copy is involved.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -31,17 +31,26 @@ extern "C" rimuru_status rimuru_expert_upload(void* pool_base, uint64_t pool_byt
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   uint8_t* pool = static_cast<uint8_t*>(pool_base);
   const uint8_t* src = static_cast<const uint8_t*>(host_src);
+  // one copy per run of pages that are consecutive in the pool as well as
+  // in the projection (the allocator gives an owner's pages from the same
+  // parent when it can, so a projection is often a few runs rather than P
+  // pages); pages past the projection's end stay unused
   for (int p = 0; p < 3; ++p) {
-    for (int32_t q = 0; q < P; ++q) {
+    const int32_t* row = pt_rows + static_cast<int64_t>(p) * P;
+    for (int32_t q = 0; q < P;) {
       const uint64_t off = static_cast<uint64_t>(q) * page_bytes;
-      if (off >= proj_bytes) break;                        // pages past the projection's end stay unused
-      const uint64_t n = proj_bytes - off < page_bytes ? proj_bytes - off : page_bytes;
-      const hipError_t err = hipMemcpyAsync(pool + static_cast<uint64_t>(pt_rows[p * P + q]) * page_bytes,
-                                            src + static_cast<uint64_t>(p) * proj_bytes + off, n,
+      if (off >= proj_bytes) break;
+      int32_t r = q + 1;
+      while (r < P && static_cast<uint64_t>(r) * page_bytes < proj_bytes && row[r] == row[r - 1] + 1) ++r;
+      const uint64_t end = static_cast<uint64_t>(r) * page_bytes < proj_bytes ? static_cast<uint64_t>(r) * page_bytes
+                                                                               : proj_bytes;
+      const hipError_t err = hipMemcpyAsync(pool + static_cast<uint64_t>(row[q]) * page_bytes,
+                                            src + static_cast<uint64_t>(p) * proj_bytes + off, end - off,
                                             hipMemcpyHostToDevice, st);
       if (err != hipSuccess)
-        return rimuru_fail(RIMURU_EHIP, "expert_upload: copy of projection %d page %d: %s", p, q,
+        return rimuru_fail(RIMURU_EHIP, "expert_upload: copy of projection %d pages %d..%d: %s", p, q, r - 1,
                            hipGetErrorString(err));
+      q = r;
     }
   }
   return RIMURU_OK;

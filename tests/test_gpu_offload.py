@@ -100,3 +100,36 @@ def test_expert_upload_into_fresh_pages():
     for p in range(3):
         R.view_free(ev, victim * 3 + p)
     R.pool_check(pool_h)
+
+
+def test_expert_upload_page_runs():
+    """Destination pages in runs of several lengths, in descending order and
+    with a partial last page: every page gets exactly its slice of the host
+    bytes, the rest of the pool (the partial page's tail included) keeps its
+    poison."""
+    page, P = 4 * KIB, 6
+    proj = 5 * page + page // 2                           # the last page half used
+    pool_bytes = 64 * page
+    rows = np.array([[10, 11, 12, 20, 21, 5],             # runs of 3, 2, 1
+                     [40, 39, 38, 37, 36, 35],            # descending: six runs of one
+                     [50, 51, 52, 53, 54, 55]],           # one run, crossing the projection's end
+                    dtype=np.int32)
+    rng = np.random.default_rng(77)
+    src = rng.integers(0, 256, size=3 * proj, dtype=np.uint8)
+    host = torch.from_numpy(src.reshape(3, proj).copy()).pin_memory()
+    dev = torch.device("cuda:0")
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pool.view(torch.int32).fill_(0x7FC07FC0)
+    poison = pool[:page].cpu().numpy().copy()
+    say("[upload] page runs: 3+2+1, six descending, one run past the projection's end")
+    side = torch.cuda.Stream()
+    R.expert_upload(pool, rows, page, host, stream=side)
+    side.synchronize()
+    got = pool.cpu().numpy()
+    expect = np.tile(poison, pool_bytes // page)
+    for p in range(3):
+        for q in range(P):
+            off = q * page
+            n = min(page, proj - off)
+            expect[rows[p, q] * page:rows[p, q] * page + n] = src[p * proj + off:p * proj + off + n]
+    assert np.array_equal(got, expect)
