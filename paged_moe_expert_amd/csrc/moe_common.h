@@ -287,9 +287,9 @@ hipError_t launch_store_pages(uint8_t* pool, uint64_t pool_bytes, const int32_t*
 // Page-table entries a streaming workgroup stages in LDS (both gated matrices).
 constexpr int kStreamPtMax = 4096;
 
-// Few rows per expert (16-row tiles): weight-streaming GEMM.
+// Few rows per expert (bm = 16, or 32 for bf16): weight-streaming GEMM.
 template <typename T, bool GATED>
-hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
+hipError_t launch_streamed(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream_t st);
 
 // Many rows per expert, bf16, 64- or 128-row tiles: the persistent pipelined
 // GEMM; hipErrorNotSupported when the shape is outside what it covers.

@@ -58,6 +58,14 @@ constexpr int kStreamNtRows = 8;
 #endif
 struct StreamShape { int bn, depth; };
 constexpr StreamShape kStreamUp{RIMURU_STREAM_UP}, kStreamDn{RIMURU_STREAM_DN};
+// the same for 32-row tiles (two 16-row blocks of accumulators)
+#ifndef RIMURU_STREAM32_UP
+#define RIMURU_STREAM32_UP 128, 2
+#endif
+#ifndef RIMURU_STREAM32_DN
+#define RIMURU_STREAM32_DN 128, 3
+#endif
+constexpr StreamShape kStream32Up{RIMURU_STREAM32_UP}, kStream32Dn{RIMURU_STREAM32_DN};
 constexpr int kStreamUpBN = kStreamUp.bn, kStreamUpDepth = kStreamUp.depth;
 constexpr int kStreamDnBN = kStreamDn.bn, kStreamDnDepth = kStreamDn.depth;
 
@@ -77,10 +85,11 @@ constexpr int stream_wave_lds() {
 // read of HBM measured 6.9 TB/s with non-temporal loads against 6.2 TB/s
 // with plain ones; taken when each expert's weights are read by one row tile
 // (few routed rows per expert), where nothing re-reads them in the launch.
-// One workgroup's tile (row tile mt, column tile nt of expert e). lds holds
+// One workgroup's tile (row tile mt of 16*MR rows, column tile nt of expert
+// e): MR blocks of 16 rows share every weight fragment. lds holds
 // kStreamMaxWaves wavefront slices of stream_wave_lds elements; pt_lds the
 // expert's page-table rows (NB * P) when not ONE_PAGE.
-template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, bool NT>
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, bool NT, int MR>
 __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int mt, int nt, int e, T* lds,
                                             int32_t* pt_lds) {
   typedef Elt<T> X;
@@ -94,8 +103,8 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
   constexpr int SEG8 = X::SEG8;
   constexpr int WL = stream_wave_lds<T, BN, GATED>();
   static_assert(CG * RG == 64 && RPL * RG == kStreamK, "stream tile shape");
-  static_assert(NB * 16 * BN * 4 <= WL * X::ES, "reduction must fit the wave buffer");
-  const int r0 = mt * 16;
+  static_assert(NB * 16 * BN * 4 <= WL * X::ES, "reduction must fit the wave buffer");   // one row block at a time
+  const int r0 = mt * 16 * MR;
   const int n0 = nt * BN;
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -104,18 +113,23 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
   const int nsteps = kw / kStreamK;
   const int kbase = wv * kw;
 
-  // A operand: row fi of the tile, K values fq*8 .. fq*8+7 of each step.
-  // Padding rows read a valid row and are zeroed by a select, so the main
-  // loop has no branch around a load (a branch there makes the compiler wait
-  // for every load in flight at the join).
-  const T* arow;
-  bool a_ok = true;
-  if (a.kdiv > 0) {
-    const int slot = a.sorted_ids[r0 + fi];
-    a_ok = slot < a.TK;
-    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(a_ok ? slot / a.kdiv : 0) * a.lda;
-  } else {
-    arow = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r0 + fi) * a.lda;
+  // A operand: row fi of each 16-row block, K values fq*8 .. fq*8+7 of each
+  // step. Padding rows read a valid row and are zeroed by a select, so the
+  // main loop has no branch around a load (a branch there makes the compiler
+  // wait for every load in flight at the join).
+  const T* arow[MR];
+  bool a_ok[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int r = r0 + 16 * m + fi;
+    a_ok[m] = true;
+    if (a.kdiv > 0) {
+      const int slot = a.sorted_ids[r];
+      a_ok[m] = slot < a.TK;
+      arow[m] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(a_ok[m] ? slot / a.kdiv : 0) * a.lda;
+    } else {
+      arow[m] = reinterpret_cast<const T*>(a.A) + static_cast<int64_t>(r) * a.lda;
+    }
   }
   const int cg = lane % CG, rg = lane / CG;
   // Page lookups read LDS: a global load here would make every weight load
@@ -139,22 +153,26 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
   const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
 
   u32x4 breg[DEPTH][NB][RPL];
-  u32x4 areg[DEPTH][SEG8];
-  f32x4 acc[NB][TN];
+  u32x4 areg[DEPTH][MR][SEG8];
+  f32x4 acc[MR][NB][TN];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[m][b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   T* wbuf = lds + wv * WL;
 
   // Loads of step st (clamped to the last step: the surplus loads at the end
   // repeat addresses already in cache and their data is never used).
-  auto issue = [&](u32x4 (&br)[NB][RPL], u32x4 (&ar)[SEG8], int st) {
+  auto issue = [&](u32x4 (&br)[NB][RPL], u32x4 (&ar)[MR][SEG8], int st) {
     st = min(st, nsteps - 1);
     const int k0 = kbase + st * kStreamK;
 #pragma unroll
-    for (int u = 0; u < SEG8; ++u) ar[u] = *reinterpret_cast<const u32x4*>(arow + k0 + fq * 8 + u * VEC);
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int u = 0; u < SEG8; ++u) ar[m][u] = *reinterpret_cast<const u32x4*>(arow[m] + k0 + fq * 8 + u * VEC);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -177,24 +195,28 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
 
   // Multiply step data into the accumulators; live == false (a step past the
   // end) multiplies by a zero A operand, which adds exact zeros.
-  auto consume = [&](const u32x4 (&br)[NB][RPL], const u32x4 (&ar)[SEG8], bool live) {
+  auto consume = [&](const u32x4 (&br)[NB][RPL], const u32x4 (&ar)[MR][SEG8], bool live) {
     // the wave's weight slice, row-major as it sits in the pool
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < RPL; ++j)
         *reinterpret_cast<u32x4*>(wbuf + b * kStreamK * BNP + (rg * RPL + j) * BNP + cg * VEC) = br[b][j];
-    const bool use = live && a_ok;
-    u32x4 af[SEG8];
+    u32x4 af[MR][SEG8];
 #pragma unroll
-    for (int u = 0; u < SEG8; ++u) af[u] = use ? ar[u] : u32x4{0u, 0u, 0u, 0u};
+    for (int m = 0; m < MR; ++m) {
+      const bool use = live && a_ok[m];
+#pragma unroll
+      for (int u = 0; u < SEG8; ++u) af[m][u] = use ? ar[m][u] : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         u32x4 bf[SEG8];
         X::bfrag16(wbuf + b * kStreamK * BNP, BNP, 0, j * 16, lane, bf);
-        acc[b][j] = X::mma8(af, bf, acc[b][j]);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m][b][j] = X::mma8(af[m], bf, acc[m][b][j]);
       }
     }
   };
@@ -223,43 +245,48 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
     }
   }
 
-  // ---- reduce the ksplit partial sums in wavefront order, then the epilogue
-  __syncthreads();
+  // ---- reduce the ksplit partial sums in wavefront order, then the
+  // epilogue, one 16-row block at a time through the wavefronts' buffers
   float* red = reinterpret_cast<float*>(wbuf);           // [NB][16][BN] of this wavefront
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[(b * 16 + 4 * fq + r) * BN + j * 16 + fi] = acc[b][j][r];
-  __syncthreads();
   constexpr int PER = 4;                                  // outputs per thread per pass
   T* C = reinterpret_cast<T*>(a.C);
-  for (int o = threadIdx.x * PER; o < 16 * BN; o += blockDim.x * PER) {
-    const int row = o / BN, col = o % BN;
-    float v[NB][PER];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    __syncthreads();                                      // buffers free: last step done, block m-1 read
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int c = 0; c < PER; ++c) v[b][c] = 0.0f;
-    for (int w = 0; w < ksplit; ++w) {
-      const float* rw = reinterpret_cast<const float*>(lds + w * WL);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(b * 16 + 4 * fq + r) * BN + j * 16 + fi] = acc[m][b][j][r];
+    __syncthreads();
+    for (int o = threadIdx.x * PER; o < 16 * BN; o += blockDim.x * PER) {
+      const int lrow = o / BN, col = o % BN;
+      const int row = r0 + 16 * m + lrow;
+      float v[NB][PER];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int c = 0; c < PER; ++c) v[b][c] += rw[(b * 16 + row) * BN + col + c];
-    }
-    if constexpr (GATED) {
-      T* dst = C + static_cast<int64_t>(r0 + row) * a.ldc + n0 + col;
+        for (int c = 0; c < PER; ++c) v[b][c] = 0.0f;
+      for (int w = 0; w < ksplit; ++w) {
+        const float* rw = reinterpret_cast<const float*>(lds + w * WL);
 #pragma unroll
-      for (int c = 0; c < PER; ++c) X::put(dst + c, silu(v[0][c]) * v[1][c]);
-    } else {
-      const int slot = a.sorted_ids[r0 + row];
-      if (slot < a.TK) {
-        const float wt = a.topk_w[slot];
-        T* dst = C + static_cast<int64_t>(slot) * a.ldc + n0 + col;
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int c = 0; c < PER; ++c) X::put(dst + c, wt * v[0][c]);
+          for (int c = 0; c < PER; ++c) v[b][c] += rw[(b * 16 + lrow) * BN + col + c];
+      }
+      if constexpr (GATED) {
+        T* dst = C + static_cast<int64_t>(row) * a.ldc + n0 + col;
+#pragma unroll
+        for (int c = 0; c < PER; ++c) X::put(dst + c, silu(v[0][c]) * v[1][c]);
+      } else {
+        const int slot = a.sorted_ids[row];
+        if (slot < a.TK) {
+          const float wt = a.topk_w[slot];
+          T* dst = C + static_cast<int64_t>(slot) * a.ldc + n0 + col;
+#pragma unroll
+          for (int c = 0; c < PER; ++c) X::put(dst + c, wt * v[0][c]);
+        }
       }
     }
   }
@@ -268,13 +295,13 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int ksplit, int m
 // NT_MODE 0: plain weight loads, 1: non-temporal, 2: per expert --
 // non-temporal when the expert's rows are one tile (nothing else in the
 // launch reads its weights), plain when several row tiles share them.
-template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, int NT_MODE>
+template <typename T, int BN, int DEPTH, bool GATED, int NSTEPS, bool ONE_PAGE, int NT_MODE, int MR>
 __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream(GemmArgs a, int ksplit) {
   __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves * stream_wave_lds<T, BN, GATED>()];
   extern __shared__ int32_t pt_lds[];          // this expert's page-table rows (NB * P)
 
   const int nN = a.N / BN;
-  const int n_tiles = a.expert_off[a.E] / 16;
+  const int n_tiles = a.expert_off[a.E] / (16 * MR);
   const int L = n_tiles * nN;
   const int chunk = (L + 7) >> 3;
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
@@ -285,12 +312,12 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   const int nt = logical - mt * nN;
   const int e = a.tile_expert[mt];
   if constexpr (NT_MODE == 2) {
-    if (a.expert_off[e + 1] - a.expert_off[e] == 16)
-      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, true>(a, ksplit, mt, nt, e, lds, pt_lds);
+    if (a.expert_off[e + 1] - a.expert_off[e] == 16 * MR)
+      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, true, MR>(a, ksplit, mt, nt, e, lds, pt_lds);
     else
-      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, false>(a, ksplit, mt, nt, e, lds, pt_lds);
+      stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, false, MR>(a, ksplit, mt, nt, e, lds, pt_lds);
   } else {
-    stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, NT_MODE == 1>(a, ksplit, mt, nt, e, lds, pt_lds);
+    stream_tile<T, BN, DEPTH, GATED, NSTEPS, ONE_PAGE, NT_MODE == 1, MR>(a, ksplit, mt, nt, e, lds, pt_lds);
   }
 }
 
@@ -298,11 +325,11 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
 
 namespace {
 
-template <typename T, int BN, int DEPTH, bool GATED, bool ONE_PAGE, int NT>
+template <typename T, int BN, int DEPTH, bool GATED, bool ONE_PAGE, int NT, int MR>
 void launch_stream_steps(int steps, dim3 gd, dim3 bd, size_t lds, hipStream_t st, const GemmArgs& g, int ksplit) {
   switch (steps) {
 #define RIMURU_STREAM_CASE(n) \
-    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n, ONE_PAGE, NT>), gd, bd, lds, st, g, ksplit); break;
+    case n: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, DEPTH, GATED, n, ONE_PAGE, NT, MR>), gd, bd, lds, st, g, ksplit); break;
     RIMURU_STREAM_CASE(2)
     RIMURU_STREAM_CASE(3)
     RIMURU_STREAM_CASE(4)
@@ -312,11 +339,11 @@ void launch_stream_steps(int steps, dim3 gd, dim3 bd, size_t lds, hipStream_t st
     RIMURU_STREAM_CASE(16)
 #undef RIMURU_STREAM_CASE
     // other step counts: runtime loop, one step less in flight (register budget)
-    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0, ONE_PAGE, NT>), gd, bd, lds, st, g, ksplit);
+    default: hipLaunchKernelGGL((k_paged_gemm_stream<T, BN, 2, GATED, 0, ONE_PAGE, NT, MR>), gd, bd, lds, st, g, ksplit);
   }
 }
 
-template <typename T, int BN, int DEPTH, bool GATED>
+template <typename T, int BN, int DEPTH, bool GATED, int MR = 1>
 hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
   const int ksteps = g.K / kStreamK;
   const int max_split = GATED ? kStreamUpWaves : kStreamDnWaves;
@@ -333,11 +360,11 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
   const bool all_nt = static_cast<int64_t>(g.TK) <= static_cast<int64_t>(kStreamNtRows) * g.E;
   const size_t pt_bytes = g.P == 1 ? 0 : static_cast<size_t>(GATED ? 2 : 1) * g.P * sizeof(int32_t);
   if (g.P == 1) {
-    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, true, 1>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
-    else launch_stream_steps<T, BN, DEPTH, GATED, true, RIMURU_STREAM_NT_MIXED>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
+    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, true, 1, MR>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
+    else launch_stream_steps<T, BN, DEPTH, GATED, true, RIMURU_STREAM_NT_MIXED, MR>(ksteps / ksplit, gd, bd, 0, st, g, ksplit);
   } else {
-    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, false, 1>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
-    else launch_stream_steps<T, BN, DEPTH, GATED, false, RIMURU_STREAM_NT_MIXED>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
+    if (all_nt) launch_stream_steps<T, BN, DEPTH, GATED, false, 1, MR>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
+    else launch_stream_steps<T, BN, DEPTH, GATED, false, RIMURU_STREAM_NT_MIXED, MR>(ksteps / ksplit, gd, bd, pt_bytes, st, g, ksplit);
   }
   return hipGetLastError();
 }
@@ -345,7 +372,23 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
 }  // namespace
 
 template <typename T, bool GATED>
-hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+hipError_t launch_streamed(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {
+  if (bm == 32) {
+    // 32-row tiles (bf16): two 16-row blocks share every weight fragment, so
+    // an expert with up to 32 routed rows reads its weights once; narrower
+    // column tiles keep the accumulators of both blocks within the register
+    // budget of two workgroups per CU
+    if constexpr (sizeof(T) == 4) {
+      return hipErrorInvalidValue;
+    } else if constexpr (GATED) {
+      if (g.N % kStream32Up.bn == 0) return launch_stream<T, kStream32Up.bn, kStream32Up.depth, true, 2>(g, tiles_max, st);
+      return launch_stream<T, 64, 3, true, 2>(g, tiles_max, st);
+    } else {
+      if (g.N % kStream32Dn.bn == 0) return launch_stream<T, kStream32Dn.bn, kStream32Dn.depth, false, 2>(g, tiles_max, st);
+      return launch_stream<T, 64, 3, false, 2>(g, tiles_max, st);
+    }
+  }
+  if (bm != 16) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 4) {
     return launch_stream<T, 64, 3, GATED>(g, tiles_max, st);
   } else {
@@ -367,9 +410,9 @@ hipError_t launch_streamed(const GemmArgs& g, uint64_t tiles_max, hipStream_t st
   }
 }
 
-template hipError_t launch_streamed<uint16_t, true>(const GemmArgs&, uint64_t, hipStream_t);
-template hipError_t launch_streamed<uint16_t, false>(const GemmArgs&, uint64_t, hipStream_t);
-template hipError_t launch_streamed<float, true>(const GemmArgs&, uint64_t, hipStream_t);
-template hipError_t launch_streamed<float, false>(const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<uint16_t, true>(int, const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<uint16_t, false>(int, const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<float, true>(int, const GemmArgs&, uint64_t, hipStream_t);
+template hipError_t launch_streamed<float, false>(int, const GemmArgs&, uint64_t, hipStream_t);
 
 }  // namespace rimuru

@@ -22,7 +22,7 @@ inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign
 
 // Tile height by expected rows per expert (T*k/E): few rows per expert is a
 // weight stream (decode), many rows is a dense grouped GEMM (prefill).
-enum PlanId { kPlan16 = 0, kPlan64 = 1, kPlan128 = 2 };
+enum PlanId { kPlan16 = 0, kPlan64 = 1, kPlan128 = 2, kPlan32 = 3 };
 struct Plan {
   PlanId id;
   int bm;
@@ -31,9 +31,19 @@ struct Plan {
 #ifndef RIMURU_PLAN64_MAX_ROWS
 #define RIMURU_PLAN64_MAX_ROWS 160
 #endif
-Plan choose_plan(int64_t T, int E, int k, int64_t P) {
+// Weight streaming up to 24 rows per expert: 16-row tiles up to 8 (most
+// experts one tile), bf16 32-row tiles above (an expert with 9 to 32 rows
+// still one tile, its weights read once: 256-token decode layer, 16 rows an
+// expert on average, half of the experts past 16).
+Plan choose_plan(int64_t T, int E, int k, int64_t P, int dtype) {
   int64_t tk = T * k;
-  if (tk <= 24ll * E && 2 * P <= kStreamPtMax) return {kPlan16, 16};
+  if (tk <= 24ll * E && 2 * P <= kStreamPtMax) {
+#ifndef RIMURU_PLAN32_MIN_ROWS
+#define RIMURU_PLAN32_MIN_ROWS 8
+#endif
+    if (dtype == RIMURU_BF16 && tk > static_cast<int64_t>(RIMURU_PLAN32_MIN_ROWS) * E) return {kPlan32, 32};
+    return {kPlan16, 16};
+  }
   if (tk <= static_cast<int64_t>(RIMURU_PLAN64_MAX_ROWS) * E) return {kPlan64, 64};
   return {kPlan128, 128};
 }
@@ -84,8 +94,9 @@ hipError_t launch_layer(const rimuru_moe_args* a, const RouterArgs* router, Plan
   hipError_t err;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   auto gemm = [&](bool gated, const GemmArgs& g) -> hipError_t {
-    if (p.id == kPlan16) return gated ? launch_streamed<T, true>(g, lay.tiles_max, st)
-                                      : launch_streamed<T, false>(g, lay.tiles_max, st);
+    if (p.id == kPlan16 || p.id == kPlan32)
+      return gated ? launch_streamed<T, true>(p.bm, g, lay.tiles_max, st)
+                   : launch_streamed<T, false>(p.bm, g, lay.tiles_max, st);
     return gated ? launch_tiled<T, true>(p.bm, g, lay.tiles_max, st)
                  : launch_tiled<T, false>(p.bm, g, lay.tiles_max, st);
   };
@@ -146,7 +157,7 @@ extern "C" rimuru_status rimuru_moe_sizes(int32_t T, int32_t E, int32_t k, int32
   rimuru_status s = check_shapes(T, E, k, H, I, dtype);
   if (s != RIMURU_OK) return s;
   if (P < 1) return rimuru_fail(RIMURU_EINVAL, "P = %d must be at least 1", P);
-  Plan p = choose_plan(T, E, k, P);
+  Plan p = choose_plan(T, E, k, P, dtype);
   Layout l = layout_for(T, E, k, H, I, dtype == RIMURU_BF16 ? 2 : 4, p.bm);
   if (sorted_len) *sorted_len = l.sorted_len;
   if (workspace_bytes) *workspace_bytes = l.total;
@@ -182,7 +193,7 @@ rimuru_status run_layer(const rimuru_moe_args* a, const RouterArgs* router, void
   if (!aligned(a->pool_base, 256) || !aligned(a->workspace, 256) || !aligned(a->x, 16) ||
       !aligned(a->y, 16) || !aligned(a->topk_ids, 16))
     return rimuru_fail(RIMURU_EINVAL, "pool_base/workspace need 256-byte and x/y/topk_ids 16-byte alignment");
-  Plan p = choose_plan(a->T, a->E, a->k, a->P);
+  Plan p = choose_plan(a->T, a->E, a->k, a->P, a->dtype);
   Layout lay = layout_for(a->T, a->E, a->k, a->H, a->I, es, p.bm);
   if (a->workspace_bytes < lay.total)
     return rimuru_fail(RIMURU_EINVAL, "workspace of %llu bytes is below the %llu needed",
@@ -271,7 +282,7 @@ extern "C" rimuru_status rimuru_fused_moe_paged_noalloc(const rimuru_moe_args* a
   if (s != RIMURU_OK) return s;
   if (a->T == 0) return RIMURU_OK;
   if (a->P < 1) return rimuru_fail(RIMURU_EINVAL, "fused_moe_paged_noalloc: P = %d must be at least 1", a->P);
-  const Plan p = choose_plan(a->T, a->E, a->k, a->P);
+  const Plan p = choose_plan(a->T, a->E, a->k, a->P, a->dtype);
   const Layout lay = layout_for(a->T, a->E, a->k, a->H, a->I, a->dtype == RIMURU_BF16 ? 2 : 4, p.bm);
   if (lay.total > RIMURU_NOALLOC_SCRATCH_BYTES)
     return rimuru_fail(RIMURU_ENOMEM, "fused_moe_paged_noalloc: this shape needs %llu bytes of workspace, above the "

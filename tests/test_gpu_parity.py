@@ -86,6 +86,11 @@ CUSTOM = [
     # the persistent GEMM on 64-row tiles (few rows per expert, weight-bound)
     ("bf16-pf64-tiles", 64, 8, 512, 256, 1000, "bf16", 8 * KIB, None),
     ("bf16-pf64-skewed-odd-page", 32, 4, 512, 512, 1200, "bf16", 12 * KIB, [3, 2, 1.5, 1] + [0] * 26 + [-2, -40]),
+    # the weight stream on 32-row tiles (9 to 24 routed rows an expert on
+    # average): a fragmented page table, and one page a projection with
+    # skewed routing (experts past 32 rows take several tiles, some none)
+    ("bf16-stream32-tiles", 16, 4, 256, 128, 80, "bf16", 4 * KIB, None),
+    ("bf16-stream32-skewed-one-page", 16, 4, 256, 128, 90, "bf16", 64 * KIB, [3, 2.5, 2] + [0] * 11 + [-40, -40]),
     # the shape limits: 512 experts, top-32 (8 logits a lane in gating, a
     # 32-row combine), with a wavefront per token and with one-workgroup routing
     ("bf16-max-experts-and-k", 512, 32, 128, 64, 50, "bf16", 4 * KIB, None),
