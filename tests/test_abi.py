@@ -53,6 +53,13 @@ def test_moe_sizes_and_plans():
     # too many pages per projection for the streaming plan: the tiled plan takes it
     _, _, bmp = R.moe_sizes(64, 128, 8, 2048, 768, 3000, R.BF16)
     assert bmp == 64
+    # streaming tile height by routed rows per expert (T*k/E): 16 up to 8,
+    # 32 (bf16) above, up to 24; fp32 streams 16-row tiles throughout
+    for T, want in ((128, 16), (129, 32), (256, 32), (384, 32), (385, 64)):
+        assert R.moe_sizes(T, 128, 8, 2048, 768, 1, R.BF16)[2] == want, T
+    assert R.moe_sizes(256, 128, 8, 2048, 768, 1, R.F32)[2] == 16
+    sl32, _, _ = R.moe_sizes(256, 128, 8, 2048, 768, 1, R.BF16)
+    assert sl32 == (2048 // 32 + 128) * 32
     with pytest.raises(_lib.RimuruError) as e:
         R.moe_sizes(4, 8, 9, 128, 64, 8, R.F32)
     assert e.value.status == _lib.EINVAL
