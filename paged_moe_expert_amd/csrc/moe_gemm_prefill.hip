@@ -145,8 +145,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // rows, chunk c holding rows 8(c/4) + c%4 and that + 4, padded to 1088
   // bytes; each copy fetches two whole 512-byte row pieces in lane order.
   // A weight segment's pool address is the address of its page (LDS, the
-  // tile context) plus its offset in the page.
-  struct Src { const uint8_t* a[S::A_DMA]; uint32_t f[S::B_DMA]; };
+  // tile context) plus its offset in the page. A tile's stages are looked up
+  // in order, so each B copy carries its segment's page index q and offset
+  // in the page r for the next stage, advanced by the stage's step
+  // (Qs pages and Rs bytes) with one compare instead of a division.
+  struct Src { const uint8_t* a[S::A_DMA]; uint32_t q[S::B_DMA], r[S::B_DMA]; };
   auto sources = [&](const Ctx& c, Src& s) {
 #pragma unroll
     for (int d = 0; d < S::A_DMA; ++d) {
@@ -165,7 +168,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
       const int b = cb / S::SUB_CHUNKS, cc = cb % S::SUB_CHUNKS;
       const int r = 8 * (cc >> 2) + (cc & 3) + 4 * (lane >> 5);
       const int col = GATED ? c.n0 + 8 * (lane & 31) : c.n0 + b * kPfSN + 8 * (lane & 31);
-      s.f[d] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(col) * 2;
+      const uint32_t f = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(col) * 2;
+      s.q[d] = page_index(f, a.pd);
+      s.r[d] = f - s.q[d] * page;
     }
   };
   // page-table row (matrix) of B copy d
@@ -176,11 +181,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
   // The page address and the offset stay apart until the copy: adding them
   // at lookup time would make the wavefront wait for the LDS read there.
   struct Refill { uint64_t pb[S::B_DMA]; uint32_t rem[S::B_DMA]; };
-  auto lookup_one = [&](const Ctx& c, const Src& s, int rst, Refill& r, int d) {
-    const uint32_t f = s.f[d] + static_cast<uint32_t>(rst) * stage_step;
-    const uint32_t q = page_index(f, a.pd);
-    r.pb[d] = c.page[bmat(d) * a.P + q];
-    r.rem[d] = f - q * page;
+  const uint32_t Qs = stage_step / page, Rs = stage_step - Qs * page;
+  auto lookup_one = [&](const Ctx& c, Src& s, Refill& r, int d) {
+    r.pb[d] = c.page[bmat(d) * a.P + s.q[d]];
+    r.rem[d] = s.r[d];
+    const uint32_t nr = s.r[d] + Rs;              // the next stage's segment: < 2 pages on
+    const bool wrap = nr >= page;
+    s.r[d] = wrap ? nr - page : nr;
+    s.q[d] += Qs + (wrap ? 1u : 0u);
   };
   auto copy_one = [&](const Src& s, const Refill& r, int rst, uint32_t buf_lds, int d) {
     if (d < S::A_DMA) {
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
     constexpr int more_k = decltype(MORE)::value;
     constexpr bool more = more_k > 0, read_next = more_k > 1;
     const Ctx& rc = ctx[(rk == 2) ? (cidx ^ 1) : cidx];
-    const Src& rs = (rk == 2) ? nxt : cur;
+    Src& rs = (rk == 2) ? nxt : cur;
     const int nbuf = buf == kPfStages - 1 ? 0 : buf + 1;
     const uint32_t buf_lds = smem_lds + buf * S::STAGE_BYTES;   // refill target: this stage's slot
     Refill rf;
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
       for (int k = tt * S::NREAD / S::NMMA; k < (tt + 1) * S::NREAD / S::NMMA; ++k) read_one(fr[1], buf, 1, k);
       if constexpr (rk != 0) {
 #pragma unroll
-        for (int d = tt * S::B_DMA / S::NMMA; d < (tt + 1) * S::B_DMA / S::NMMA; ++d) lookup_one(rc, rs, rst, rf, d);
+        for (int d = tt * S::B_DMA / S::NMMA; d < (tt + 1) * S::B_DMA / S::NMMA; ++d) lookup_one(rc, rs, rf, d);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
 #pragma unroll
     for (int st = 0; st < kPfStages; ++st) {
 #pragma unroll
-      for (int d = 0; d < S::B_DMA; ++d) lookup_one(ctx[0], cur, st, rf, d);
+      for (int d = 0; d < S::B_DMA; ++d) lookup_one(ctx[0], cur, rf, d);
 #pragma unroll
       for (int d = 0; d < S::DMA; ++d) copy_one(cur, rf, st, smem_lds + st * S::STAGE_BYTES, d);
     }
@@ -456,8 +464,12 @@ hipError_t launch_prefill(int bm, const GemmArgs& g, uint64_t tiles_max, hipStre
   const uint64_t tiles = tiles_max * static_cast<uint64_t>(g.N / bnw);
   uint64_t grid = std::min<uint64_t>(static_cast<uint64_t>(cu_count() / 8 * 8), (tiles + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
+#ifndef RIMURU_PF128_NW
+#define RIMURU_PF128_NW 8
+#endif
   if (bm == 128)
-    hipLaunchKernelGGL((k_moe_gemm_pf<GATED, 8, 128>), dim3(static_cast<uint32_t>(grid)), dim3(8 * 64), 0, st, g);
+    hipLaunchKernelGGL((k_moe_gemm_pf<GATED, RIMURU_PF128_NW, 128>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(RIMURU_PF128_NW * 64), 0, st, g);
   else if constexpr (!GATED)
     hipLaunchKernelGGL((k_moe_gemm_pf<GATED, 4, 64>), dim3(static_cast<uint32_t>(grid)), dim3(4 * 64), 0, st, g);
   return hipGetLastError();
