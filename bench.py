@@ -36,7 +36,8 @@ KERNEL_SOURCES = {"stream": ("moe_common.h", "moe_gemm_stream.hip"),
                   "tiled": ("moe_common.h", "moe_gemm_tiled.hip"),
                   "prefill": ("moe_common.h", "moe_gemm_prefill.hip")}
 # GEMM kernel family (gate/up, down) of each tile height
-KIND_OF_BLOCK_M = {16: ("stream", "stream"), 32: ("stream", "stream"), 64: ("tiled", "prefill"), 128: ("prefill", "prefill")}
+KIND_OF_BLOCK_M = {16: ("stream", "stream"), 32: ("stream", "stream"), 64: ("tiled", "prefill"),
+                   128: ("prefill", "prefill")}
 STAGES = ["gating", "count", "sort", "gemm_up", "gemm_down", "combine"]
 
 
