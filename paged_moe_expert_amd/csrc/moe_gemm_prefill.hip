@@ -25,6 +25,10 @@ constexpr int kPfSN = 256;        // columns of one weight sub-tile (512-byte ro
 constexpr int kPfBK = 32;         // K rows per stage
 constexpr int kPfStages = 3;      // stages in the LDS ring
 constexpr int kPfCtxPages = 1024; // page addresses a tile context holds
+#ifndef RIMURU_PF_PRE
+#define RIMURU_PF_PRE 2
+#endif
+constexpr int kPfPre = RIMURU_PF_PRE;  // second-K-step MFMAs issued before a stage's barrier
 
 template <int NW, int BM>
 struct PfShape {
@@ -287,8 +291,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    mma(fr[1], 0);
-    mma(fr[1], 1);
+    constexpr int PRE = kPfPre;                   // MFMAs of the second K step before the barrier
+#pragma unroll
+    for (int tt = 0; tt < PRE; ++tt) mma(fr[1], tt);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (more) {
       wait_lds();
@@ -297,16 +302,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_moe_gemm_pf(GemmArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int tt = 2; tt < S::NMMA; ++tt) {
+    for (int tt = PRE; tt < S::NMMA; ++tt) {
       mma(fr[1], tt);
-      constexpr int R = S::NMMA - 2;
+      constexpr int R = S::NMMA - PRE;
       if constexpr (read_next) {
 #pragma unroll
-        for (int k = (tt - 2) * S::NREAD / R; k < (tt - 1) * S::NREAD / R; ++k) read_one(fr[0], nbuf, 0, k);
+        for (int k = (tt - PRE) * S::NREAD / R; k < (tt - PRE + 1) * S::NREAD / R; ++k) read_one(fr[0], nbuf, 0, k);
       }
       if constexpr (rk != 0) {
 #pragma unroll
-        for (int d = (tt - 2) * S::DMA / R; d < (tt - 1) * S::DMA / R; ++d) copy_one(rs, rf, rst, buf_lds, d);
+        for (int d = (tt - PRE) * S::DMA / R; d < (tt - PRE + 1) * S::DMA / R; ++d) copy_one(rs, rf, rst, buf_lds, d);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
