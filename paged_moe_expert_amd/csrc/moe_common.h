@@ -268,6 +268,10 @@ struct RouterArgs {
   float* logits_out;
 };
 
+// Slot-list ranges the count and sort of many routed slots are cut into (the
+// counts buffer holds E * kCountSplits entries).
+constexpr int kCountSplits = 8;
+
 // Routing (gating top-k, per-expert sort padded to bm-row tiles) on stream st;
 // counts/tile_expert live in the workspace. router == null: top-k of the given
 // logits; else the logits are computed from x and w_gate first. Stage marks 1

@@ -59,7 +59,7 @@ Layout layout_for(int64_t T, int E, int k, int H, int I, int es, int bm) {
   l.tiles_max = static_cast<uint64_t>(tk / bm + (tk < E ? tk : E));
   l.sorted_len = l.tiles_max * bm;
   l.off_counts = 0;
-  l.off_tiles = align_up(static_cast<uint64_t>(E) * 4);
+  l.off_tiles = align_up(static_cast<uint64_t>(E) * kCountSplits * 4);   // counts [E][splits]
   l.off_logits = l.off_tiles + align_up(l.tiles_max * 4);        // router logits [T, E] fp32
   l.off_h = l.off_logits + align_up(static_cast<uint64_t>(T) * E * 4);
   l.off_yslot = l.off_h + align_up(l.sorted_len * static_cast<uint64_t>(I) * es);

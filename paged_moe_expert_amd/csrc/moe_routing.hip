@@ -415,15 +415,26 @@ void launch_router(const RouterArgs& r, int n_tok, int E, hipStream_t st) {
 
 // ---------------------------------------------------------------- stage 2: count
 
-// ids is 16-byte aligned (validated); 8 independent 16-byte loads per thread
-// are in flight per round.
+// The slot list is cut into gridDim.y consecutive ranges of a multiple of 4
+// slots; workgroup (e, s) counts expert e's slots in range s into
+// counts[e * S + s] (several workgroups per expert when there are few
+// experts, so that every CU scans). ids is 16-byte aligned (validated); 8
+// independent 16-byte loads per thread are in flight per round.
+__device__ __forceinline__ void slot_range(int TK, int s, int S, int* lo, int* hi) {
+  const int per = ((TK + S - 1) / S + 3) & ~3;
+  *lo = min(s * per, TK);
+  *hi = min(*lo + per, TK);
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_count(const int32_t* __restrict__ ids, int TK,
                                               int32_t* __restrict__ counts) {
   __shared__ int part[NT / 64];
-  const int e = blockIdx.x;
-  const int n4 = TK >> 2;
-  const u32x4* v = reinterpret_cast<const u32x4*>(ids);
+  const int e = blockIdx.x, s = blockIdx.y, S = gridDim.y;
+  int lo, hi;
+  slot_range(TK, s, S, &lo, &hi);
+  const int n4 = (hi - lo) >> 2;
+  const u32x4* v = reinterpret_cast<const u32x4*>(ids + lo);
   const uint32_t ue = static_cast<uint32_t>(e);
   int c = 0;
   for (int base = 0; base < n4; base += NT * 8) {
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(NT) void k_count(const int32_t* __restrict__ ids, i
     for (int u = 0; u < 8; ++u)
       c += (r[u][0] == ue) + (r[u][1] == ue) + (r[u][2] == ue) + (r[u][3] == ue);
   }
-  for (int f = n4 * 4 + threadIdx.x; f < TK; f += NT) c += (ids[f] == e);
+  for (int f = lo + n4 * 4 + threadIdx.x; f < hi; f += NT) c += (ids[f] == e);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
@@ -446,7 +457,7 @@ __global__ __launch_bounds__(NT) void k_count(const int32_t* __restrict__ ids, i
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < NT / 64; ++i) sum += part[i];
-    counts[e] = sum;
+    counts[e * S + s] = sum;
   }
 }
 
@@ -481,6 +492,10 @@ constexpr int kSortChunk = 64;  // consecutive slots per thread per round (16 x 
 // LDS (small batches: this saves the separate count launch).
 constexpr int kSortSelfCountMax = 4096;   // routed slots
 
+// Workgroup (e, s) places expert e's slots of range s (the ranges of
+// k_count, gridDim.y of them): after the slots of the earlier ranges, so the
+// segment stays in ascending slot order. The last range's workgroup pads the
+// segment and writes its tiles' expert, the first the segment's start.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ ids, int TK, int E,
                                                    int BM, const int32_t* __restrict__ counts,
@@ -489,20 +504,27 @@ __global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ i
                                                    int32_t* __restrict__ tile_expert) {
   __shared__ int sh[NT / 64];
   __shared__ int hist[kMaxE];
-  const int e = blockIdx.x;
+  const int e = blockIdx.x, s = blockIdx.y, S = gridDim.y;
   const int tid = threadIdx.x;
   const uint32_t ue = static_cast<uint32_t>(e);
+  int cs = S;                                     // counts of expert e2: cnt_of(e2) sums its S ranges
   if (counts == nullptr) {
     for (int i = tid; i < E; i += NT) hist[i] = 0;
     __syncthreads();
     for (int f = tid; f < TK; f += NT) atomicAdd(&hist[ids[f]], 1);
     __syncthreads();
     counts = hist;
+    cs = 1;
   }
+  auto cnt_of = [&](int e2) {
+    int c = 0;
+    for (int j = 0; j < cs; ++j) c += counts[e2 * cs + j];
+    return c;
+  };
   // start of this expert's padded segment, and the padded total
   int before = 0, total = 0;
   for (int e2 = tid; e2 < E; e2 += NT) {
-    int pc = (counts[e2] + BM - 1) / BM * BM;
+    int pc = (cnt_of(e2) + BM - 1) / BM * BM;
     total += pc;
     before += (e2 < e) ? pc : 0;
   }
@@ -510,21 +532,25 @@ __global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ i
   block_excl_scan<NT>(before, &sum_before, sh);   // block sums of the per-thread partials
   block_excl_scan<NT>(total, &sum_total, sh);
   const int seg = sum_before;
-  const int cnt = counts[e];
-  if (tid == 0) {
+  const int cnt = cnt_of(e);
+  int earlier = 0;                                // this expert's slots in the ranges before s
+  for (int j = 0; j < s; ++j) earlier += counts[e * cs + j];
+  if (tid == 0 && s == 0) {
     expert_off[e] = seg;
     if (e == 0) expert_off[E] = sum_total;
   }
+  int lo = 0, hi = TK;
+  if (cs > 1) slot_range(TK, s, S, &lo, &hi);
   const bool vec = (TK & 3) == 0;
   int running = 0;
-  for (int base = 0; base < TK; base += NT * kSortChunk) {
+  for (int base = lo; base < hi; base += NT * kSortChunk) {
     const int f0 = base + tid * kSortChunk;
     uint64_t mask = 0;
     if (vec) {
       u32x4 r[kSortChunk / 4];
 #pragma unroll
       for (int u = 0; u < kSortChunk / 4; ++u)
-        r[u] = (f0 + 4 * u < TK) ? *reinterpret_cast<const u32x4*>(ids + f0 + 4 * u)
+        r[u] = (f0 + 4 * u < hi) ? *reinterpret_cast<const u32x4*>(ids + f0 + 4 * u)
                                  : u32x4{~0u, ~0u, ~0u, ~0u};
 #pragma unroll
       for (int u = 0; u < kSortChunk / 4; ++u)
@@ -533,11 +559,11 @@ __global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ i
     } else {
       for (int i = 0; i < kSortChunk; ++i) {
         const int f = f0 + i;
-        if (f < TK && ids[f] == e) mask |= 1ull << i;
+        if (f < hi && ids[f] == e) mask |= 1ull << i;
       }
     }
     int chunk_total;
-    int pos = seg + running + block_excl_scan<NT>(__popcll(mask), &chunk_total, sh);
+    int pos = seg + earlier + running + block_excl_scan<NT>(__popcll(mask), &chunk_total, sh);
     while (mask) {
       const int i = __ffsll(static_cast<long long>(mask)) - 1;
       sorted_ids[pos++] = f0 + i;
@@ -545,9 +571,11 @@ __global__ __launch_bounds__(NT) void k_sort_align(const int32_t* __restrict__ i
     }
     running += chunk_total;
   }
-  const int padded = (cnt + BM - 1) / BM * BM;
-  for (int i = cnt + tid; i < padded; i += NT) sorted_ids[seg + i] = TK;
-  for (int i = tid; i < padded / BM; i += NT) tile_expert[seg / BM + i] = e;
+  if (s == S - 1) {
+    const int padded = (cnt + BM - 1) / BM * BM;
+    for (int i = cnt + tid; i < padded; i += NT) sorted_ids[seg + i] = TK;
+    for (int i = tid; i < padded / BM; i += NT) tile_expert[seg / BM + i] = e;
+  }
 }
 
 // ---------------------------------------------------------------- stages 1-3 for small batches
@@ -772,19 +800,22 @@ hipError_t launch_routing(const float* logits, const RouterArgs* router, int T, 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if ((err = mark(1)) != hipSuccess) return err;
   const bool self_count = TK <= kSortSelfCountMax;
-  if (!self_count) {
-    // many slots: 1024 threads a workgroup, so each expert's scan over all
-    // slots takes a quarter of the rounds
-    hipLaunchKernelGGL(k_count<1024>, dim3(E), dim3(1024), 0, st, topk_ids, TK, counts);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  if ((err = mark(2)) != hipSuccess) return err;
-  if (self_count)
+  if (self_count) {
+    if ((err = mark(2)) != hipSuccess) return err;
     hipLaunchKernelGGL(k_sort_align<256>, dim3(E), dim3(256), 0, st, topk_ids, TK, E, bm, nullptr, sorted_ids,
                        expert_off, tile_expert);
-  else
-    hipLaunchKernelGGL(k_sort_align<1024>, dim3(E), dim3(1024), 0, st, topk_ids, TK, E, bm, counts, sorted_ids,
-                       expert_off, tile_expert);
+    return hipGetLastError();
+  }
+  // many slots: the slot list is cut into S ranges (up to kCountSplits) so
+  // that a 256-thread workgroup's sort covers its range in one round, and
+  // E * S small workgroups scan in parallel
+  int S = 1;
+  while (S < kCountSplits && static_cast<int64_t>(S) * 256 * kSortChunk < TK) S *= 2;
+  hipLaunchKernelGGL(k_count<256>, dim3(E, S), dim3(256), 0, st, topk_ids, TK, counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = mark(2)) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_sort_align<256>, dim3(E, S), dim3(256), 0, st, topk_ids, TK, E, bm, counts, sorted_ids,
+                     expert_off, tile_expert);
   return hipGetLastError();
 }
 

@@ -91,6 +91,9 @@ CUSTOM = [
     # skewed routing (experts past 32 rows take several tiles, some none)
     ("bf16-stream32-tiles", 16, 4, 256, 128, 80, "bf16", 4 * KIB, None),
     ("bf16-stream32-skewed-one-page", 16, 4, 256, 128, 90, "bf16", 64 * KIB, [3, 2.5, 2] + [0] * 11 + [-40, -40]),
+    # count and sort of many slots cut into ranges (two here), with T*k not a
+    # multiple of 4 (the unvectorised scans)
+    ("bf16-split-sort-odd-slots", 8, 3, 128, 64, 5001, "bf16", 4 * KIB, None),
     # the shape limits: 512 experts, top-32 (8 logits a lane in gating, a
     # 32-row combine), with a wavefront per token and with one-workgroup routing
     ("bf16-max-experts-and-k", 512, 32, 128, 64, 50, "bf16", 4 * KIB, None),
