@@ -381,7 +381,11 @@ hipError_t launch_streamed(int bm, const GemmArgs& g, uint64_t tiles_max, hipStr
     if constexpr (sizeof(T) == 4) {
       return hipErrorInvalidValue;
     } else if constexpr (GATED) {
-      if (g.N % kStream32Up.bn == 0) return launch_stream<T, kStream32Up.bn, kStream32Up.depth, true, 2>(g, tiles_max, st);
+      // projections over several pages: the per-segment page lookups need
+      // registers the 128-column tile's accumulators leave no room for (it
+      // spills), so those take 64 columns
+      if (g.P == 1 && g.N % kStream32Up.bn == 0)
+        return launch_stream<T, kStream32Up.bn, kStream32Up.depth, true, 2>(g, tiles_max, st);
       return launch_stream<T, 64, 3, true, 2>(g, tiles_max, st);
     } else {
       if (g.N % kStream32Dn.bn == 0) return launch_stream<T, kStream32Dn.bn, kStream32Dn.depth, false, 2>(g, tiles_max, st);
