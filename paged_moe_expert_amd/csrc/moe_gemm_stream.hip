@@ -407,13 +407,16 @@ hipError_t launch_streamed(int bm, const GemmArgs& g, uint64_t tiles_max, hipStr
       if (enough(64, kStreamNarrow.up_bn)) return launch_stream<T, 64, 3, true>(g, tiles_max, st);
       return launch_stream<T, 32, 3, true>(g, tiles_max, st);
     } else {
-      // projections over several pages with more than 8 steps a wavefront
-      // (the K split as launch_stream takes it): the page lookups need
-      // registers the 256-column tile leaves no room for (it spills), the
-      // 128-column one does not
+      // projections over several pages with more than 8 steps a wavefront,
+      // or a step count the K loop is not unrolled for (the K split as
+      // launch_stream takes it): the page lookups need registers the
+      // 256-column tile leaves no room for (it spills), the 128-column one
+      // does not
       const int ksteps = g.K / kStreamK;
       const int ksplit = (ksteps % 4 == 0 && kStreamDnWaves >= 4) ? 4 : (ksteps % 2 == 0 && kStreamDnWaves >= 2) ? 2 : 1;
-      const bool long_k = g.P > 1 && ksteps / ksplit > 8;
+      const int wsteps = ksteps / ksplit;
+      const bool unrolled = wsteps == 2 || wsteps == 3 || wsteps == 4 || wsteps == 6 || wsteps == 8;
+      const bool long_k = g.P > 1 && !unrolled;
       if (!long_k && enough(kStreamDnBN, kStreamNarrow.dn_bn))
         return launch_stream<T, kStreamDnBN, kStreamDnDepth, false>(g, tiles_max, st);
       if (enough(128, kStreamNarrow.dn_bn)) return launch_stream<T, 128, 3, false>(g, tiles_max, st);
