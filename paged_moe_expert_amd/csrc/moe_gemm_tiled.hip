@@ -4,6 +4,8 @@
 // abstract and Figure 11, "Discrete FusedMoE"; Table 1 for the projections).
 //   gemm-up    h = SiLU(x w1) * (x w3)
 //   gemm-down  y_slot[t*k+j] = w[t,j] * (h w2)
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace rimuru {
@@ -109,114 +111,127 @@ __global__ __launch_bounds__(WM* WN * 64) void k_paged_gemm(GemmArgs a) {
   const uint32_t col_bytes = static_cast<uint32_t>(n0 + cb * VEC) * X::ES;
   const uint32_t row_bytes = static_cast<uint32_t>(a.N) * X::ES;
 
-  u32x4 a_reg[A_LOADS];
-  u32x4 b_reg[NB][RK];
+  // Weights of an expert whose routed rows fit one row tile are read by no
+  // other tile of the launch at these columns: they stream past the caches
+  // (non-temporal loads, bf16). Several row tiles of one expert share them
+  // in L2 instead (plain loads).
+  const bool nt_tile = sizeof(T) == 2 && a.expert_off[e + 1] - a.expert_off[e] == BM;
+  auto run = [&](auto NTC) {
+    constexpr bool NTW = decltype(NTC)::value;
+    u32x4 a_reg[A_LOADS];
+    u32x4 b_reg[NB][RK];
 
-  auto load_stage = [&](int kt) {
+    auto load_stage = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
+      for (int i = 0; i < A_LOADS; ++i) a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
-      for (int j = 0; j < RK; ++j) {
-        const uint32_t f = static_cast<uint32_t>(kt * BK + rb * RK + j) * row_bytes + col_bytes;
-        const uint32_t q = page_index(f, a.pd);
-        const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
-        b_reg[b][j] = *reinterpret_cast<const u32x4*>(p);
+        for (int j = 0; j < RK; ++j) {
+          const uint32_t f = static_cast<uint32_t>(kt * BK + rb * RK + j) * row_bytes + col_bytes;
+          const uint32_t q = page_index(f, a.pd);
+          const uint8_t* p = a.pool + static_cast<uint64_t>(pt_row[b][q]) * a.pd.page + (f - q * a.pd.page);
+          if constexpr (NTW)
+            b_reg[b][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+          else
+            b_reg[b][j] = *reinterpret_cast<const u32x4*>(p);
+        }
       }
-    }
-  };
+    };
 
-  auto store_stage = [&](int buf) {
+    auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      if (tid + i * NT < A_SEGS) {
-        const u32x4 v = a_ok[i] ? a_reg[i] : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&As[buf][a_row[i] * BKP + a_kv[i] * VEC]) = v;
+      for (int i = 0; i < A_LOADS; ++i) {
+        if (tid + i * NT < A_SEGS) {
+          const u32x4 v = a_ok[i] ? a_reg[i] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&As[buf][a_row[i] * BKP + a_kv[i] * VEC]) = v;
+        }
       }
-    }
-    // weight rows as they are: 16-byte segments, row pitch BNP
+      // weight rows as they are: 16-byte segments, row pitch BNP
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < RK; ++j)
+          *reinterpret_cast<u32x4*>(&Bs[buf][b][(rb * RK + j) * BNP + cb * VEC]) = b_reg[b][j];
+    };
+
+    f32x16 acc[NB][TM][TN];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int j = 0; j < RK; ++j)
-        *reinterpret_cast<u32x4*>(&Bs[buf][b][(rb * RK + j) * BNP + cb * VEC]) = b_reg[b][j];
-  };
-
-  f32x16 acc[NB][TM][TN];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
-
-  const int nk = a.K / BK;
-  const int fi = lane & 31, fq = lane >> 5;  // operand row/column and K half of this lane
-
-  if constexpr (PT_LDS) __syncthreads();
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = (NBUF == 2) ? (kt & 1) : 0;
-    if (kt + 1 < nk) load_stage(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / KI; ++kk) {
-      typename X::Frag af[TM], bfr[NB][TN];
-#pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = X::frag(&As[buf][(wm * WTM + i * 32 + fi) * BKP + kk * KI + fq * FE]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[b][j] = X::bfrag32(Bs[buf][b], BNP, kk * KI, wn * WTN + j * 32, lane);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+          for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
+
+    const int nk = a.K / BK;
+    const int fi = lane & 31, fq = lane >> 5;  // operand row/column and K half of this lane
+
+    if constexpr (PT_LDS) __syncthreads();
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = (NBUF == 2) ? (kt & 1) : 0;
+      if (kt + 1 < nk) load_stage(kt + 1);
+#pragma unroll
+      for (int kk = 0; kk < BK / KI; ++kk) {
+        typename X::Frag af[TM], bfr[NB][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
+          af[i] = X::frag(&As[buf][(wm * WTM + i * 32 + fi) * BKP + kk * KI + fq * FE]);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[b][i][j] = X::mma32(af[i], bfr[b][j], acc[b][i][j]);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bfr[b][j] = X::bfrag32(Bs[buf][b], BNP, kk * KI, wn * WTN + j * 32, lane);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[b][i][j] = X::mma32(af[i], bfr[b][j], acc[b][i][j]);
+      }
+      if constexpr (NBUF == 2) {
+        if (kt + 1 < nk) store_stage(buf ^ 1);
+        __syncthreads();
+      } else if (kt + 1 < nk) {
+        __syncthreads();
+        store_stage(0);
+        __syncthreads();
+      }
     }
-    if constexpr (NBUF == 2) {
-      if (kt + 1 < nk) store_stage(buf ^ 1);
-      __syncthreads();
-    } else if (kt + 1 < nk) {
-      __syncthreads();
-      store_stage(0);
-      __syncthreads();
-    }
-  }
 
-  // ---- epilogue: acc[r] of a 32x32 tile is row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
-  T* C = reinterpret_cast<T*>(a.C);
+    // ---- epilogue: acc[r] of a 32x32 tile is row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
+    T* C = reinterpret_cast<T*>(a.C);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
-      if constexpr (GATED) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WTN + j * 32 + fi;
-          X::put(&C[static_cast<int64_t>(row) * a.ldc + col], silu(acc[0][i][j][r]) * acc[1][i][j][r]);
-        }
-      } else {
-        const int slot = a.sorted_ids[row];
-        if (slot < a.TK) {
-          const float wt = a.topk_w[slot];
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
+        if constexpr (GATED) {
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int col = n0 + wn * WTN + j * 32 + fi;
-            X::put(&C[static_cast<int64_t>(slot) * a.ldc + col], wt * acc[0][i][j][r]);
+            X::put(&C[static_cast<int64_t>(row) * a.ldc + col], silu(acc[0][i][j][r]) * acc[1][i][j][r]);
+          }
+        } else {
+          const int slot = a.sorted_ids[row];
+          if (slot < a.TK) {
+            const float wt = a.topk_w[slot];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int col = n0 + wn * WTN + j * 32 + fi;
+              X::put(&C[static_cast<int64_t>(slot) * a.ldc + col], wt * acc[0][i][j][r]);
+            }
           }
         }
       }
     }
-  }
+  };
+  if (nt_tile) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------- bf16, many rows: asynchronous pipeline
