@@ -83,6 +83,12 @@ CUSTOM = [
     ("bf16-pf-many-tiles", 8, 2, 512, 256, 40000, "bf16", 4 * KIB, None),
     ("bf16-pf-short-k", 4, 2, 192, 256, 3000, "bf16", 4 * KIB, None),
     ("bf16-pf-skewed-odd-page", 16, 4, 512, 512, 20000, "bf16", 12 * KIB, [4, 3, 2.5, 2, 1] + [0] * 9 + [-3, -50]),
+    # the 128-row asynchronous-pipeline GEMM, where the persistent one does
+    # not take the shape: gate/up over 768 pages a projection (more page
+    # addresses than a persistent tile context holds), and a down GEMM of
+    # K = 128 (four 32-deep stages, fewer than the persistent ring needs)
+    ("bf16-pipelined-long-page-table", 8, 2, 1024, 1536, 1000, "bf16", 4 * KIB, None),
+    ("bf16-pipelined-short-down", 8, 2, 512, 128, 1200, "bf16", 4 * KIB, None),
     # the persistent GEMM on 64-row tiles (few rows per expert, weight-bound)
     ("bf16-pf64-tiles", 64, 8, 512, 256, 1000, "bf16", 8 * KIB, None),
     ("bf16-pf64-skewed-odd-page", 32, 4, 512, 512, 1200, "bf16", 12 * KIB, [3, 2, 1.5, 1] + [0] * 26 + [-2, -40]),
