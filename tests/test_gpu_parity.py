@@ -97,6 +97,9 @@ CUSTOM = [
     # skewed routing (experts past 32 rows take several tiles, some none)
     ("bf16-stream32-tiles", 16, 4, 256, 128, 80, "bf16", 4 * KIB, None),
     ("bf16-stream32-skewed-one-page", 16, 4, 256, 128, 90, "bf16", 64 * KIB, [3, 2.5, 2] + [0] * 11 + [-40, -40]),
+    # the 16-row weight stream's down GEMM over many pages with 12 steps a
+    # wavefront (K = 1536), where it takes 128-column tiles
+    ("bf16-decode-long-down", 64, 4, 512, 1536, 64, "bf16", 4 * KIB, None),
     # count and sort of many slots cut into ranges (two here), with T*k not a
     # multiple of 4 (the unvectorised scans)
     ("bf16-split-sort-odd-slots", 8, 3, 128, 64, 5001, "bf16", 4 * KIB, None),
