@@ -362,7 +362,13 @@ typedef struct {
 } rimuru_moe_args;
 
 /* Stages, in launch order: gating top-k, per-expert count, sort + tile align,
- * gate/up GEMM with SiLU, down GEMM with routing weight, top-k combine. */
+ * gate/up GEMM with SiLU, down GEMM with routing weight, top-k combine. Some
+ * stages share a kernel, and then the events around the later ones are
+ * recorded back to back: the count runs inside the sort up to 4096 routed
+ * slots, one kernel routes batches of up to 16 tokens, and for bf16 batches
+ * of at most 4 tokens (16-row tiles, given logits, H a multiple of 128) the
+ * gate/up stream does the routing itself, whose time then falls in the
+ * gate/up stage. */
 #define RIMURU_MOE_STAGES 6
 
 /* Buffer sizes for a call with these shapes and P pages per projection:

@@ -5,6 +5,7 @@
 #include <algorithm>
 
 #include "moe_common.h"
+#include "moe_topk.h"
 
 namespace rimuru {
 
@@ -321,6 +322,94 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   }
 }
 
+// Gate/up stream of a tiny batch (at most kRoutedMaxT tokens) with the
+// routing done in the same launch: every workgroup selects the top-k of each
+// token and builds the per-expert lists in its own LDS (the same lists in
+// every workgroup, as the separate routing kernels would write them), then
+// takes its tile from that copy; workgroup 0 also writes the lists and the
+// top-k out for the down GEMM, the combine and the caller. This removes the
+// routing launch, the largest fixed cost of a one-token layer.
+template <typename T, int BN, int DEPTH, int NSTEPS, bool ONE_PAGE>
+__global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void k_paged_gemm_stream_routed(
+    GemmArgs a, int ksplit, TinyRoute rt) {
+  __shared__ __attribute__((aligned(16))) T lds[kStreamMaxWaves * stream_wave_lds<T, BN, true>()];
+  extern __shared__ int32_t pt_lds[];
+  __shared__ int32_t s_ids[kRoutedMaxTK];
+  __shared__ float s_w[kRoutedMaxTK];
+  __shared__ int32_t s_off[kRoutedMaxE + 1];
+  __shared__ int32_t s_sorted[kRoutedMaxSorted];
+  __shared__ int32_t s_tile[kRoutedMaxSorted / 16];
+  __shared__ int s_scan[kStreamMaxWaves];
+  constexpr int EPL = kRoutedMaxE / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.E, k = rt.k, TK = a.TK;
+
+  // top-k of token wv (one wavefront a token)
+  if (wv < rt.T) {
+    float v[EPL];
+    load_logits<EPL>(rt.logits + static_cast<int64_t>(wv) * E, E, lane, v);
+    uint32_t e;
+    float wt;
+    select_topk_vals<EPL>(v, E, k, lane, &e, &wt);
+    if (lane < k) {
+      s_ids[wv * k + lane] = static_cast<int32_t>(e);
+      s_w[wv * k + lane] = wt;
+    }
+  }
+  __syncthreads();
+  // per-expert segments padded to 16 rows (one expert a thread), their
+  // starts by a block scan, then every slot at its rank among its expert's
+  // earlier slots (ascending slot order, the stable grouping)
+  const int cnt_e = [&] {
+    int c = 0;
+    if (tid < E)
+      for (int f = 0; f < TK; ++f) c += s_ids[f] == tid;
+    return c;
+  }();
+  const int padded = (cnt_e + 15) / 16 * 16;
+  int total;
+  const int seg = block_excl_scan<kStreamMaxWaves * 64>(padded, &total, s_scan);
+  if (tid < E) {
+    s_off[tid] = seg;
+    for (int i = cnt_e; i < padded; ++i) s_sorted[seg + i] = TK;
+    for (int i = 0; i < padded / 16; ++i) s_tile[seg / 16 + i] = tid;
+  }
+  if (tid == 0) s_off[E] = total;
+  __syncthreads();
+  if (tid < TK) {
+    const int my = s_ids[tid];
+    int rank = 0;
+    for (int f = 0; f < tid; ++f) rank += s_ids[f] == my;
+    s_sorted[s_off[my] + rank] = tid;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < TK) {
+      rt.topk_ids[tid] = s_ids[tid];
+      rt.topk_w[tid] = s_w[tid];
+    }
+    for (int i = tid; i < total; i += blockDim.x) rt.sorted_ids[i] = s_sorted[i];
+    for (int i = tid; i <= E; i += blockDim.x) rt.expert_off[i] = s_off[i];
+    for (int i = tid; i < total / 16; i += blockDim.x) rt.tile_expert[i] = s_tile[i];
+  }
+
+  // this workgroup's tile, as the stream kernel maps them
+  const int nN = a.N / BN;
+  const int L = (total / 16) * nN;
+  const int chunk = (L + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  if (idx >= chunk) return;
+  const int logical = xcd * chunk + idx;
+  if (logical >= L) return;
+  const int mt = logical / nN;
+  const int nt = logical - mt * nN;
+  GemmArgs g = a;
+  g.sorted_ids = s_sorted;
+  g.expert_off = s_off;
+  g.tile_expert = s_tile;
+  stream_tile<T, BN, DEPTH, true, NSTEPS, ONE_PAGE, true, 1>(g, ksplit, mt, nt, s_tile[mt], lds, pt_lds);
+}
+
 // ---------------------------------------------------------------- launchers
 
 namespace {
@@ -369,7 +458,58 @@ hipError_t launch_stream(const GemmArgs& g, uint64_t tiles_max, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <typename T, int BN, int DEPTH>
+hipError_t launch_routed(const GemmArgs& g, uint64_t tiles_max, const TinyRoute& rt, hipStream_t st) {
+  const uint64_t blocks = tiles_max * static_cast<uint64_t>(g.N / BN);
+  const uint64_t grid = (blocks + 7) / 8 * 8;
+  const dim3 gd(static_cast<uint32_t>(grid)), bd(kStreamMaxWaves * 64);
+  const size_t pt_bytes = g.P == 1 ? 0 : static_cast<size_t>(2) * g.P * sizeof(int32_t);
+  const int ksplit = kStreamMaxWaves;
+  const bool unrolled = g.K / kStreamK / ksplit == 16;
+  if (g.P == 1) {
+    if (unrolled) hipLaunchKernelGGL((k_paged_gemm_stream_routed<T, BN, DEPTH, 16, true>), gd, bd, 0, st, g, ksplit, rt);
+    else hipLaunchKernelGGL((k_paged_gemm_stream_routed<T, BN, 2, 0, true>), gd, bd, 0, st, g, ksplit, rt);
+  } else {
+    if (unrolled) hipLaunchKernelGGL((k_paged_gemm_stream_routed<T, BN, DEPTH, 16, false>), gd, bd, pt_bytes, st, g, ksplit, rt);
+    else hipLaunchKernelGGL((k_paged_gemm_stream_routed<T, BN, 2, 0, false>), gd, bd, pt_bytes, st, g, ksplit, rt);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The routed stream needs all four wavefronts for the routing (a token each,
+// one thread an expert), so it takes shapes whose K splits four ways; the
+// column tile is chosen as for the 16-row stream. Every slot's weight loads
+// are non-temporal (a tiny batch reads each expert's weights once).
+bool streamed_routed_fits(int dtype_bytes, int T, int k, int E, int K, uint64_t tiles_max) {
+  // at most 4 tokens: an expert gets at most 4 rows, one 16-row tile, so
+  // the padded lists hold at most 16 rows a touched expert (<= 512)
+  const int TK = T * k;
+  return dtype_bytes == 2 && T >= 1 && T <= kRoutedMaxT && TK <= kRoutedMaxTK && E <= kRoutedMaxE &&
+         K % (kStreamK * kStreamMaxWaves) == 0 && kStreamUpWaves >= kStreamMaxWaves &&
+         tiles_max >= static_cast<uint64_t>(std::min(TK, E));
+}
+
+template <typename T>
+hipError_t launch_streamed_routed(const GemmArgs& g, uint64_t tiles_max, const TinyRoute& rt, hipStream_t st) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorNotSupported;
+  } else {
+    if (g.TK != rt.T * rt.k || !streamed_routed_fits(2, rt.T, rt.k, g.E, g.K, tiles_max)) return hipErrorNotSupported;
+    const int64_t touched = std::min<int64_t>(g.E, g.TK);
+    auto enough = [&](int bn, int floor_bn) {
+      return g.N % bn == 0 && (bn <= floor_bn || touched * (g.N / bn) >= kStreamNarrow.min_groups);
+    };
+    if (enough(kStreamUpBN, kStreamNarrow.up_bn)) return launch_routed<T, kStreamUpBN, kStreamUpDepth>(g, tiles_max, rt, st);
+    if (enough(64, kStreamNarrow.up_bn)) return launch_routed<T, 64, 3>(g, tiles_max, rt, st);
+    if (g.N % 32 == 0) return launch_routed<T, 32, 3>(g, tiles_max, rt, st);
+    return hipErrorNotSupported;
+  }
+}
+
+template hipError_t launch_streamed_routed<uint16_t>(const GemmArgs&, uint64_t, const TinyRoute&, hipStream_t);
+template hipError_t launch_streamed_routed<float>(const GemmArgs&, uint64_t, const TinyRoute&, hipStream_t);
 
 template <typename T, bool GATED>
 hipError_t launch_streamed(int bm, const GemmArgs& g, uint64_t tiles_max, hipStream_t st) {

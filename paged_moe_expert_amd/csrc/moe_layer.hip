@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "moe_common.h"
+#include "moe_topk.h"
 
 namespace rimuru {
 namespace {
@@ -101,10 +102,17 @@ hipError_t launch_layer(const rimuru_moe_args* a, const RouterArgs* router, Plan
                  : launch_tiled<T, false>(p.bm, g, lay.tiles_max, st);
   };
 
+  // a tiny batch on 16-row tiles with given logits: the gate/up stream
+  // routes it itself (one launch less); its time then counts as gate/up
+  const bool routed = p.id == kPlan16 && router == nullptr &&
+                      streamed_routed_fits(static_cast<int>(sizeof(T)), T_, k, E, H, lay.tiles_max);
   if ((err = mark(0)) != hipSuccess) return err;
-  if ((err = launch_routing(a->logits, router, T_, E, k, p.bm, a->topk_ids, a->topk_w, counts, a->sorted_ids,
-                            a->expert_off, tile_expert, ev, st)) != hipSuccess)
+  if (routed) {
+    if ((err = mark(1)) != hipSuccess || (err = mark(2)) != hipSuccess) return err;
+  } else if ((err = launch_routing(a->logits, router, T_, E, k, p.bm, a->topk_ids, a->topk_w, counts, a->sorted_ids,
+                                   a->expert_off, tile_expert, ev, st)) != hipSuccess) {
     return err;
+  }
 
   GemmArgs g{};
   g.sorted_ids = a->sorted_ids;
@@ -126,7 +134,12 @@ hipError_t launch_layer(const rimuru_moe_args* a, const RouterArgs* router, Plan
   g.N = I;
   g.C = h;
   g.ldc = I;
-  if ((err = gemm(true, g)) != hipSuccess) return err;
+  if (routed) {
+    const TinyRoute rt{a->logits, T_, k, a->topk_ids, a->topk_w, a->sorted_ids, a->expert_off, tile_expert};
+    if ((err = launch_streamed_routed<T>(g, lay.tiles_max, rt, st)) != hipSuccess) return err;
+  } else if ((err = gemm(true, g)) != hipSuccess) {
+    return err;
+  }
 
   if ((err = mark(4)) != hipSuccess) return err;
   g.A = h;

@@ -139,13 +139,16 @@ def test_custom_shapes_against_oracle(spec):
     assert torch.equal(b2.y, bufs.y)
 
 
-@pytest.mark.parametrize("T", [8, 40, 4096], ids=["one-workgroup-routing", "gating-and-sort", "gating-count-sort"])
+@pytest.mark.parametrize("T", [3, 8, 40, 4096],
+                         ids=["routing-in-gate-up-stream", "one-workgroup-routing", "gating-and-sort", "gating-count-sort"])
 def test_tied_and_signed_zero_logits(T):
     """Logits drawn from {-1, -0.0, +0.0, 0.5, 1} (seeded): most tokens have
     ties at the top-k boundary and between -0 and +0. The kernels must keep
     the lower expert index on a tie and treat -0 as +0, exactly as the
-    oracle's route does (8 tokens: one-workgroup routing; 40: gating and the
-    self-counting sort; 4096: gating, count and sort)."""
+    oracle's route does (3 tokens: the gate/up stream routes the batch
+    itself, over several pages a projection; 8 tokens: one-workgroup
+    routing; 40: gating and the self-counting sort; 4096: gating, count and
+    sort)."""
     E, k, H, I, page = 16, 4, 256, 128, 4 * KIB
     name = f"bf16-ties-T{T}"
     cfg, P, n_pages, pt, wb, xb, _ = _custom(name, E, k, H, I, T, "bf16", page, seed=50 + T)
