@@ -340,10 +340,23 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   __shared__ int32_t s_sorted[kRoutedMaxSorted];
   __shared__ int32_t s_tile[kRoutedMaxSorted / 16];
   __shared__ int s_scan[kStreamMaxWaves];
+  __shared__ int32_t s_pt[3 * kRoutedMaxE];
   constexpr int EPL = kRoutedMaxE / 64;
+  constexpr int PTJ = 3 * kRoutedMaxE / (kStreamMaxWaves * 64);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, k = rt.k, TK = a.TK;
 
+  // one page a projection: every expert's page-table row (3 entries) is read
+  // together with the logits and kept in LDS, so no workgroup waits on a
+  // global read for its weights' page after the selection
+  int32_t ptv[PTJ];
+  if constexpr (ONE_PAGE) {
+#pragma unroll
+    for (int j = 0; j < PTJ; ++j) {
+      const int i = tid + j * kStreamMaxWaves * 64;
+      ptv[j] = i < 3 * E ? a.pt[i] : 0;
+    }
+  }
   // top-k of token wv (one wavefront a token)
   if (wv < rt.T) {
     float v[EPL];
@@ -354,6 +367,13 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
     if (lane < k) {
       s_ids[wv * k + lane] = static_cast<int32_t>(e);
       s_w[wv * k + lane] = wt;
+    }
+  }
+  if constexpr (ONE_PAGE) {
+#pragma unroll
+    for (int j = 0; j < PTJ; ++j) {
+      const int i = tid + j * kStreamMaxWaves * 64;
+      if (i < 3 * E) s_pt[i] = ptv[j];
     }
   }
   __syncthreads();
@@ -407,6 +427,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64, RIMURU_STREAM_WG_PER_CU) void
   g.sorted_ids = s_sorted;
   g.expert_off = s_off;
   g.tile_expert = s_tile;
+  if constexpr (ONE_PAGE) g.pt = s_pt;
   stream_tile<T, BN, DEPTH, true, NSTEPS, ONE_PAGE, true, 1>(g, ksplit, mt, nt, s_tile[mt], lds, pt_lds);
 }
 
