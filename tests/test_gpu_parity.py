@@ -69,6 +69,10 @@ CUSTOM = [
     ("bf16-one-expert", 1, 1, 192, 64, 50, "bf16", 4 * KIB, None),
     ("bf16-128B-pages", 4, 2, 64, 64, 21, "bf16", 128, None),
     ("bf16-one-token", 16, 4, 256, 128, 1, "bf16", 4 * KIB, None),
+    # 4 tokens x 8 experts of 40 on one 64 KiB page a projection: the gate/up
+    # stream routes the batch itself with the page table staged in LDS, and
+    # the expert count is not a multiple of the 64 lanes that select
+    ("bf16-routed-stream-one-page", 40, 8, 256, 128, 4, "bf16", 64 * KIB, None),
     # 24576 pages per projection: too many to stage in LDS, read from global
     ("bf16-huge-page-table", 2, 1, 2048, 768, 300, "bf16", 128, None),
     ("bf16-huge-page-table-decode", 2, 1, 2048, 768, 8, "bf16", 128, None),
