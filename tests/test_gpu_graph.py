@@ -5,9 +5,10 @@ then one graph launch instead of several kernel launches from the host.
 
 Each replay gets new inputs written into the captured x and logits buffers,
 with eager work and synchronisations between replays, and its outputs must
-equal those of an eager call on the same inputs bitwise. Cases: 8 tokens
-(one-workgroup routing, weight streaming), 40 tokens (gating + sort,
-weight streaming) and 300 tokens (64-row tiled GEMMs).
+equal those of an eager call on the same inputs bitwise. Cases: 3 tokens
+(the gate/up stream routes the batch itself), 8 tokens (one-workgroup
+routing, weight streaming), 40 tokens (gating + sort, weight streaming) and
+300 tokens (64-row tiled GEMMs).
 """
 from dataclasses import replace
 
@@ -25,7 +26,7 @@ if torch.cuda.is_available():
     from paged_moe_expert_amd import rimuru as R
 
 
-@pytest.mark.parametrize("T", [8, 40, 300])
+@pytest.mark.parametrize("T", [3, 8, 40, 300])
 def test_graph_replay_equals_eager(T):
     E, k, H, I, page = 16, 4, 256, 128, 4 * KIB
     cfg = replace(CFG1, cid=400 + T, name=f"bf16-graph-T{T}", E=E, k=k, H=H, I=I, T=T, dtype="bf16",
